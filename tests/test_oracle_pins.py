@@ -1,0 +1,245 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compare the oracle with itself: each checks it against an
+independent definition (numpy's IEEE conversions and reductions, histograms,
+closed forms, values printed on the pages, or the fp64 exhaustive search in
+oracle/brute.py).
+"""
+import os
+
+import numpy as np
+import pytest
+
+from ggml_iq_codebook_imatrix_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FORMATS = ("IQ2_XXS", "IQ2_XS", "IQ2_S", "IQ1_S", "IQ1_M")
+
+
+# --------------------------------------------------------------------------
+# Format geometry (sizes printed on the pages)
+# --------------------------------------------------------------------------
+def test_block_geometry_matches_pages(orc):
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "block_geometry.txt")) if l.strip() and not l.startswith("#")]
+    for name, nbytes, bpw, n in rows:
+        geo = orc.geometry(name)
+        assert geo["block_bytes"] == int(nbytes)
+        assert geo["block_bytes"] * 8 / 256 == pytest.approx(float(bpw))
+        assert geo["grid_n"] == int(n)
+    # choice ranges: IQ2 [0, 16) (4-bit scale field); IQ1 "16-choice or 8-choice"
+    assert [orc.geometry(f)["num_choices"] for f in FORMATS] == [16, 16, 16, 16, 8]
+    # one local scale per 32 values (IQ2_XXS, IQ1_S) or per 16 values (IQ2_XS, IQ2_S, IQ1_M)
+    assert [orc.geometry(f)["groups_per_unit"] * 8 for f in FORMATS] == [32, 16, 16, 32, 16]
+
+
+# --------------------------------------------------------------------------
+# fp16 conversion against numpy's IEEE round-to-nearest-even
+# --------------------------------------------------------------------------
+def test_f16_conversion_matches_numpy(orc):
+    g = inputs.rng(7)
+    vals = np.concatenate([
+        g.standard_normal(4000).astype(np.float32) * np.float32(10.0) ** g.integers(-9, 5, 4000).astype(np.float32),
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, 6e-8, 5.96e-8, 2.98e-8, 2.99e-8, 1e-10,
+                  6.1035156e-05, 6.097555e-05, 0.0625, 0.0625082, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11],
+                 dtype=np.float32),
+    ]).astype(np.float32)
+    # exact ties on the fp16 grid at several binades, both parities
+    base = np.float16(np.arange(1, 500)).astype(np.float32)
+    ulp = np.spacing(np.float16(np.arange(1, 500))).astype(np.float32)
+    vals = np.concatenate([vals, base + ulp / 2, (base + ulp / 2) * np.float32(2 ** -20)]).astype(np.float32)
+    ours = orc.f32_to_f16_bits(vals)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = orc.f16_bits_to_f32(ref[np.isfinite(ref.view(np.float16))])
+    assert np.array_equal(back, ref[np.isfinite(ref.view(np.float16))].view(np.float16).astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# Packing: round trip over every field value, and the layout facts the pages print
+# --------------------------------------------------------------------------
+FIELD_RANGES = {  # (index bits, has 8-bit mask, has parity-coded mask, has h, ls range)
+    "IQ2_XXS": (8, True, True, False, 16),
+    "IQ2_XS": (9, True, True, False, 16),
+    "IQ2_S": (10, True, False, False, 16),
+    "IQ1_S": (11, False, False, True, 8),
+    "IQ1_M": (11, False, False, True, 8),
+}
+
+
+def _random_fields(fmt, g):
+    bits, has_mask, parity, has_h, nls = FIELD_RANGES[fmt]
+    geo = {"IQ2_XXS": 8, "IQ2_XS": 16, "IQ2_S": 16, "IQ1_S": 8, "IQ1_M": 16}[fmt]
+    f = dict(d=int(g.integers(0, 1 << 16)), k=g.integers(0, 1 << bits, 32), mask=np.zeros(32, int),
+             h=np.zeros(32, int), ls=np.zeros(16, int))
+    if has_mask:
+        m = g.integers(0, 256, 32)
+        if parity:  # even popcount: bit 7 = parity of bits 0..6
+            m = (m & 0x7F) | (np.array([bin(v & 0x7F).count("1") & 1 for v in m]) << 7)
+        f["mask"] = m
+    f["ls"][:geo] = g.integers(0, nls, geo)
+    if has_h:
+        if fmt == "IQ1_S":  # one shift per 32-value sub-block
+            f["h"] = np.repeat(g.integers(0, 2, 8), 4)
+        else:
+            f["h"] = g.integers(0, 2, 32)
+    return f
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_pack_unpack_round_trip(orc, fmt):
+    g = inputs.rng(11)
+    for _ in range(300):
+        f = _random_fields(fmt, g)
+        b = orc.pack_fields(fmt, f)
+        u = orc.unpack_fields(fmt, b)
+        assert u["d"] == f["d"]
+        assert np.array_equal(u["k"], f["k"])
+        assert np.array_equal(u["mask"], f["mask"])
+        assert np.array_equal(u["h"], f["h"])
+        assert np.array_equal(u["ls"], f["ls"])
+        assert np.array_equal(orc.pack_fields(fmt, u), b)
+
+
+def test_iq2_xxs_word_layout(orc):
+    """ModelOpt PR #2513, IQ2_XXS message: four 7-bit sign indices and a 4-bit
+    sub-block scale share one 32-bit word; the 256-entry grid needs no high bits."""
+    f = dict(d=0x3C00, k=np.arange(32) * 7 % 256, mask=np.zeros(32, int), h=np.zeros(32, int),
+             ls=np.zeros(16, int))
+    f["mask"][4:8] = [0b10000001, 0b00000011, 0b01111111 | 0b10000000, 0]   # even parity
+    f["ls"][1] = 13
+    b = orc.pack_fields("IQ2_XXS", f)
+    word = int.from_bytes(bytes(b[2 + 8 + 4:2 + 8 + 8]), "little")
+    assert word >> 28 == 13
+    assert [(word >> (7 * l)) & 0x7F for l in range(4)] == [0b0000001, 0b0000011, 0b1111111, 0]
+    assert list(b[2 + 8:2 + 12]) == list(f["k"][4:8])
+
+
+def test_iq1_m_scale_from_nibbles_and_pairs(orc):
+    """ModelOpt PR #2513, IQ1_M body: no leading d field; fp16 d is the top nibble of
+    each of four scale words; one 3-bit local scale per two groups, expanded as
+    [h0, h0, h1, h1] (the decoder bug that body describes)."""
+    grid = np.zeros((2048, 8), np.float32)
+    grid[0] = 1.0
+    f = dict(d=0x2C00, k=np.zeros(32, int), mask=np.zeros(32, int), h=np.zeros(32, int),
+             ls=np.arange(16) % 8)
+    b = orc.pack_fields("IQ1_M", f)
+    nib = [int.from_bytes(bytes(b[48 + 2 * w:50 + 2 * w]), "little") >> 12 for w in range(4)]
+    assert sum(n << (4 * w) for w, n in enumerate(nib)) == 0x2C00
+    y = orc.dequantize("IQ1_M", b[None, None, :], 1, 256, grid)[0]
+    s = np.float32(0.0625) * (2 * (np.arange(16) % 8) + 1).astype(np.float32)
+    expect = np.repeat(s * np.float32(1.125), 16)  # scale u covers groups 2u, 2u+1 = 16 values
+    assert np.array_equal(y, expect.astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# Collection: closed form (numpy fp64) and histogram of the routing ids
+# --------------------------------------------------------------------------
+def test_collect_dense_closed_form(orc):
+    x = inputs.activations(300, 96, 1, 2, bf16=True)
+    sums, counts, st = orc.collect(x)
+    assert st == 0 and counts[0] == 300
+    ref = np.square(x.astype(np.float64)).sum(axis=0)
+    assert np.allclose(sums[0], ref, rtol=1e-14, atol=0)
+
+
+def test_collect_moe_histogram_and_sums(orc):
+    T, K, E, top_k = 257, 40, 16, 3
+    x = inputs.activations(T, K, 3, 4, bf16=True)
+    ids = inputs.routing(T, top_k, E, 5, n_idle=2)
+    sums, counts, st = orc.collect(x, ids, E)
+    assert st == 0
+    assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+    assert (counts == 0).sum() >= 2
+    for e in range(E):  # brute force: tokens whose top-k holds e, each occurrence once
+        mult = (ids == e).sum(axis=1).astype(np.float64)
+        ref = (mult[:, None] * np.square(x.astype(np.float64))).sum(axis=0)
+        assert np.allclose(sums[e], ref, rtol=1e-13, atol=0)
+    # a token routed twice to one expert counts twice
+    ids2 = ids.copy()
+    ids2[0] = [1, 1, 2]
+    _, c2, _ = orc.collect(x, ids2, E)
+    assert c2[1] == np.bincount(ids2.ravel(), minlength=E)[1]
+
+
+def test_collect_flags_nonfinite_and_bad_ids(orc):
+    x = np.ones((4, 8), np.float32)
+    x[2, 3] = np.inf
+    _, _, st = orc.collect(x)
+    assert st & orc.ST_NONFINITE
+    ids = np.array([[0], [1], [5], [1]], np.int32)
+    _, counts, st = orc.collect(np.ones((4, 8), np.float32), ids, 3)
+    assert st & orc.ST_BADID and counts.tolist() == [1, 2, 0]
+
+
+# --------------------------------------------------------------------------
+# Importance: closed form of the floored square root, flat for idle experts
+# --------------------------------------------------------------------------
+def test_importance_closed_form(orc):
+    g = inputs.rng(9)
+    K = 512
+    sums = (g.lognormal(0, 2, (4, K)) * 100).astype(np.float32)
+    sums[2, :7] = 0.0                      # dead columns hit the floor
+    counts = np.array([100, 0, 37, 1], np.int64)
+    imp, st = orc.importance(sums, counts, 1e-6)
+    assert st == 0
+    assert np.all(imp[1] == 1.0)           # count 0 -> weight 1 on every channel
+    for e in (0, 2, 3):
+        m = (sums[e] / np.float32(counts[e])).astype(np.float32)
+        mean = np.float32(m.astype(np.float64).sum() / K)
+        fl = np.float32(np.float32(1e-6) * mean)
+        ref = np.sqrt(np.maximum(m, fl)).astype(np.float32)
+        assert np.array_equal(imp[e], ref)
+    assert np.all(imp[2, :7] > 0)
+    # all-zero statistic with count > 0: nothing usable -> flat
+    imp2, _ = orc.importance(np.zeros((1, 8), np.float32), np.array([5]), 1e-6)
+    assert np.all(imp2 == 1.0)
+
+
+# --------------------------------------------------------------------------
+# Anchor: closed forms and the IQ1_M clamp special cases
+# --------------------------------------------------------------------------
+def test_anchor_closed_forms(orc):
+    g = inputs.rng(13)
+    x = (g.standard_normal(256) * 0.02).astype(np.float32)
+    amax = np.abs(x).max()
+    f16 = lambda v: int(np.float32(v).astype(np.float16).view(np.uint16))
+    # IQ2: d = amax / (3.875 * 5)
+    for fmt in ("IQ2_XXS", "IQ2_XS", "IQ2_S"):
+        assert orc.anchor(fmt, x)[0] == f16(np.float32(amax) / np.float32(19.375))
+    # IQ1_S: flat 0.61 (ModelOpt PR #2513 IQ1_M body, "against IQ1_S's flat 0.61")
+    assert orc.anchor("IQ1_S", x)[0] == f16((np.float32(0.61) * amax) / np.float32(15.0))
+    # IQ1_M: constant magnitude -> peak/rms = 1 -> ratio clamps to 0.65
+    c = np.full(256, 0.5, np.float32)
+    c[::3] *= -1
+    assert orc.anchor("IQ1_M", c)[0] == f16(np.float32(0.65) * np.float32(0.5) / np.float32(15))
+    # one spike -> peak/rms = 16 -> 0.58 + 0.56 = 1.14 clamps to 0.95
+    s = np.zeros(256, np.float32)
+    s[77] = -2.0
+    assert orc.anchor("IQ1_M", s)[0] == f16(np.float32(0.95) * np.float32(2.0) / np.float32(15))
+    # in between: ratio = 0.58 + 0.035 * p exactly where no clamp applies
+    v = np.zeros(256, np.float32)
+    v[:16] = 1.0                            # rms = 1/4, p = 4 -> 0.72
+    assert orc.anchor("IQ1_M", v)[0] == f16(np.float32(0.72) * np.float32(1.0) / np.float32(15))
+
+
+def test_anchor_zero_nonfinite_overflow(orc):
+    z = np.zeros(256, np.float32)
+    for fmt in FORMATS:
+        assert orc.anchor(fmt, z) == (0, 0)
+        n = z.copy()
+        n[5] = np.nan
+        h, st = orc.anchor(fmt, n)
+        assert h == 0 and st & orc.ST_NONFINITE
+        big = z.copy()
+        big[0] = 3e7
+        h, st = orc.anchor(fmt, big)
+        assert h == 0 and st & orc.ST_OVERFLOW
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_zero_block_gives_zero_payload(orc, fmt):
+    """ModelOpt PR #3157 review: an all-zero block comes out as an all-zero payload."""
+    grid = inputs.grid_for(fmt, 201)
+    out, st = orc.encode_block(fmt, np.zeros(256, np.float32), np.ones(256, np.float32), grid)
+    assert st == 0 and not out.any()
