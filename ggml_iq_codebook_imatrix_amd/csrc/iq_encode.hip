@@ -1,0 +1,690 @@
+// iq_encode.hip -- importance-weighted GGML IQ encoder and decoder for gfx950.
+//
+// What is computed (pages cited by title and section):
+//  * ModelOpt PR #2513, commit messages: every 256-value block gets a fixed
+//    anchored fp16 super-block scale d, then a single-pass search of the grid;
+//    IQ2_XXS / IQ2_XS use an even-parity 7-bit sign index and flip the weakest
+//    element to fix parity; IQ2_S keeps the input signs and compares
+//    magnitudes; IQ1 values carry a +-1/8 delta, IQ1_S per 32 values, IQ1_M per
+//    group with ties going to the lower shift, then the lower entry; IQ1_M's
+//    anchor ratio is clamp(0.58 + 0.035 * peak_to_rms, 0.65, 0.95), IQ1_S's 0.61.
+//  * ModelOpt PR "[1/5] Let the GGML IQ encoders take fixed per-group choices":
+//    each choice unit takes the local scale (IQ1_S: and delta sign) with the
+//    least importance-weighted squared error; given choices, only the entry
+//    search runs; an all-zero block gives an all-zero payload.
+//  * "Add imatrix calibration for the GGML formats ...", description: the
+//    search weight of column j is a_j = sqrt(E[x_j^2]).
+//
+// Arithmetic.  For a group of 8 values x_j with weights a_j, entry g_k and
+// local scale s, the weighted error is sum a_j (y_j - s u_j)^2 =
+// sum a_j y_j^2 + s (s G - 2 P) with G = sum a_j u_j^2, P = sum a_j y_j u_j.
+// The search ranks t = fmaf(s, G, -2P) (fp32, contraction off, explicit fmaf);
+// per (group, slot) it keeps the first minimum over entries, each choice unit
+// takes the choice with the least sum over its groups of s * t_min (left to
+// right, lowest choice on ties).
+//  IQ2: y = |x|, u = g; -2P is the fmaf chain of (-2 a_j y_j) * g_kj; with an odd
+//       number of negative inputs (IQ2_XXS/XS) the cheapest single flip
+//       F = min_j a_j y_j g_kj is charged: -2P' = fmaf(4, F, -2P).
+//  IQ1: y = x, u = g + delta (delta = +1/8 for shift 0, -1/8 for shift 1);
+//       -2P = fmaf(delta, S, Q) with Q the fmaf chain of (-2 a_j x_j) g_kj and
+//       S = sum (-2 a_j x_j), i.e. per-entry grid terms plus one shift term.
+//
+// gfx950 design.  One wave per 8-value group and 64 rows per wave: the grid
+// entry and the weighted norm G_k are then the same for all 64 lanes, so they
+// arrive as scalar loads (SGPR operands) and cost no VGPRs or LDS bandwidth;
+// G_k is precomputed once per (expert, column group) by gterm_kernel.  The
+// sweep keeps, per slot, a running minimum per 16-entry chunk (v_min3 pairs)
+// and the index of the chunk holding the first minimum; after the unit's
+// choice is known the chosen chunk is rescanned to recover the exact entry.
+// A workgroup holds the groups whose payload bytes nobody else writes (one
+// 32-value sub-block; IQ1_M: 64 values), exchanges per-slot minima through LDS
+// to score its choice units, and packs its bytes itself.
+
+#include "iq_common.hpp"
+#include "iq_internal.hpp"
+
+namespace iq {
+
+// ---------------------------------------------------------------------------
+// Workgroup order: the hardware deals consecutive workgroups round robin to the
+// 8 XCDs.  Remap so each XCD gets a contiguous range of logical work (the same
+// column groups over all their row tiles), which keeps each column group's
+// weighted-norm table in one XCD's L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total) {
+  const int64_t q = total >> 3, r = total & 7;
+  const int64_t x = i & 7, j = i >> 3;
+  return x * q + (x < r ? x : r) + j;
+}
+
+// ---------------------------------------------------------------------------
+// Anchor: one thread per block.  Writes the fp16 scale bits (0 = all-zero
+// block) to dscr and, for layouts with a leading d field, to the payload.
+// ---------------------------------------------------------------------------
+template <int F>
+__global__ void __launch_bounds__(256) anchor_kernel(EncArgs A) {
+  using G = Geo<F>;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= A.rows * A.nb) return;
+  const int64_t r = i / A.nb;
+  const int b = static_cast<int>(i % A.nb);
+  const int64_t e = r / A.rpe;
+  const int64_t base = r * A.cols + static_cast<int64_t>(b) * 256;
+  int st = 0;
+  float amax = 0.0f;
+  bool finite = true;
+  for (int j8 = 0; j8 < 32; ++j8) {
+    float v[8];
+    load8(A.w, A.dtype, base + 8 * j8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      finite = finite && finite_f(v[j]);
+      amax = fmaxf(amax, fabsf(v[j]));
+    }
+  }
+  uint16_t h = 0;
+  if (!finite) {
+    st |= ST_NONFINITE;
+  } else if (amax > 0.0f) {
+    float ratio = 1.0f;                 // IQ2: no ratio is printed on the pages; 1
+    if (F == IQ1_S) ratio = 0.61f;
+    if (F == IQ1_M) {                   // peak-to-RMS over the 256-value block
+      float ss = 0.0f;
+      for (int j8 = 0; j8 < 32; ++j8) {
+        float v[8];
+        load8(A.w, A.dtype, base + 8 * j8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
+      }
+      const float rms = sqrtf(ss * (1.0f / 256.0f));
+      const float p = amax / rms;
+      ratio = fminf(fmaxf(__builtin_fmaf(0.035f, p, 0.58f), 0.65f), 0.95f);
+    }
+    const float qmax = G::IQ1 ? 15.0f : 19.375f;  // top multiplier * top magnitude
+    const float d = (ratio * amax) / qmax;
+    h = f32_to_f16_bits(d);
+    if ((h & 0x7c00u) == 0x7c00u) {
+      st |= ST_OVERFLOW;
+      h = 0;
+    } else if ((h & 0x7fffu) == 0) {
+      h = 0;
+    }
+  }
+  if (A.imp) {
+    const float *ap = A.imp + e * A.cols + static_cast<int64_t>(b) * 256;
+    bool ok = true;
+    for (int j = 0; j < 256; j += 4) {
+      const float4 q = *reinterpret_cast<const float4 *>(ap + j);
+      ok = ok && finite_f(q.x) && finite_f(q.y) && finite_f(q.z) && finite_f(q.w) &&
+           q.x >= 0.0f && q.y >= 0.0f && q.z >= 0.0f && q.w >= 0.0f;
+    }
+    if (!ok) { st |= ST_BADIMP; h = 0; }
+  }
+  if (A.choices) {
+    const uint8_t *cp = A.choices + i * G::UNITS;
+    bool ok = true;
+    for (int u = 0; u < G::UNITS; ++u) ok = ok && cp[u] < G::NC;
+    if (!ok) { st |= ST_BADCHOICE; h = 0; }
+  }
+  A.dscr[i] = h;
+  if (F != IQ1_M) *reinterpret_cast<uint16_t *>(A.out + i * G::BYTES) = h;
+  raise_status(A.status, st);
+}
+
+// ---------------------------------------------------------------------------
+// Weighted norms of every grid entry for one (expert, column group):
+// IQ2: G_k = sum_j a_j g_kj^2;  IQ1: G^h_k = sum_j a_j (g_kj + delta_h)^2.
+// Thread per (table, entry).  Flat weights use a single table (a_j = 1).
+// ---------------------------------------------------------------------------
+template <int F>
+__global__ void __launch_bounds__(256) gterm_kernel(const float *__restrict__ grid,
+                                                     const float *__restrict__ imp, int64_t cols,
+                                                     int64_t ntab, float *__restrict__ gtab) {
+  using G = Geo<F>;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= ntab * G::N) return;
+  const int k = static_cast<int>(i % G::N);
+  const int64_t tab = i / G::N;  // = e * (cols / 8) + cg
+  float a[8], g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = imp ? imp[tab * 8 + j] : 1.0f;  // importance row e, columns 8cg..8cg+7
+    g[j] = grid[static_cast<int64_t>(k) * 8 + j];
+  }
+  if (!G::IQ1) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = __builtin_fmaf(a[j], g[j] * g[j], s);
+    gtab[tab * G::N + k] = s;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float delta = h ? -0.125f : 0.125f;
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float u = g[j] + delta;
+        s = __builtin_fmaf(a[j], u * u, s);
+      }
+      gtab[(tab * 2 + h) * G::N + k] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-lane group state and the per-entry reduced errors.
+// ---------------------------------------------------------------------------
+template <int F>
+struct GroupState {
+  float ax[8];   // IQ2: a_j |x_j|
+  float nax[8];  // IQ2: -2 a_j |x_j| ; IQ1: -2 a_j x_j
+  float f4;      // IQ2 parity: 4 for an odd count of negative inputs, else 0
+  float S2;      // IQ1: sum_j -2 a_j x_j
+  uint32_t neg;  // IQ2: negative mask
+  bool odd;
+
+  __device__ __forceinline__ void init(const float x[8], const float a[8]) {
+    neg = 0;
+    S2 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!Geo<F>::IQ1) {
+        const float v = fabsf(x[j]);
+        neg |= (x[j] < 0.0f ? 1u : 0u) << j;
+        ax[j] = a[j] * v;
+        nax[j] = -2.0f * ax[j];
+      } else {
+        ax[j] = 0.0f;
+        nax[j] = -2.0f * (a[j] * x[j]);
+        S2 = S2 + nax[j];
+      }
+    }
+    odd = Geo<F>::PARITY && (__builtin_popcount(neg) & 1);
+    f4 = odd ? 4.0f : 0.0f;
+  }
+
+  // IQ2: -2 P'_k for grid entry g;  IQ1: Q_k (before the shift term)
+  __device__ __forceinline__ float term(const float g[8]) const {
+    float p = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p = __builtin_fmaf(nax[j], g[j], p);
+    if (Geo<F>::PARITY) {
+      float fm = ax[0] * g[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) fm = fminf(fm, ax[j] * g[j]);
+      p = __builtin_fmaf(f4, fm, p);
+    }
+    return p;
+  }
+
+  // element flipped to fix parity for entry g: the first j with least a_j |x_j| g_j
+  __device__ __forceinline__ int flip_index(const float g[8]) const {
+    int jm = 0;
+    float fm = ax[0] * g[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      const float f = ax[j] * g[j];
+      if (f < fm) { fm = f; jm = j; }
+    }
+    return jm;
+  }
+};
+
+__device__ __forceinline__ void load_entry(const float *p, float g[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+  g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// Search + pack.  Workgroup = WGG waves (groups) x 64 rows of one expert.
+// ---------------------------------------------------------------------------
+template <int F, bool FIXED>
+__global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
+  using G = Geo<F>;
+  constexpr int WGG = G::WGG, GPU = G::GPU, N = G::N;
+  constexpr int CH = 16, NCH = N / CH;
+  constexpr int UPW = WGG / GPU;                 // choice units per workgroup
+  constexpr int SBS = 32 / WGG;                  // workgroups per block column
+  // slots swept per lane: IQ2 16 choices; IQ1 8 scales x 2 shifts;
+  // fixed choices: one slot (IQ1_M: its two shifts)
+  constexpr int NSLOT = FIXED ? (F == IQ1_M ? 2 : 1) : 16;
+
+  __shared__ float s_best[FIXED ? 1 : WGG][FIXED ? 1 : NSLOT][64];
+  __shared__ uint16_t s_k[WGG][64];
+  __shared__ uint8_t s_m[WGG][64];
+  __shared__ uint8_t s_c[UPW][64];
+
+  const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
+  const int64_t tile = L % A.tiles_per_e;
+  const int64_t q = L / A.tiles_per_e;
+  const int colset = static_cast<int>(q % (static_cast<int64_t>(A.nb) * SBS));
+  const int64_t e = q / (static_cast<int64_t>(A.nb) * SBS);
+  const int b = colset / SBS, sb = colset % SBS;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t rin = tile * 64 + lane;
+  const bool valid = rin < A.rpe;
+  const int64_t r = e * A.rpe + (valid ? rin : A.rpe - 1);
+  const int gi = sb * WGG + wave;                  // group within the block
+  const int64_t cg = static_cast<int64_t>(b) * 32 + gi;
+  const int uw = wave / GPU;                       // unit within the workgroup
+  const int unit = gi / GPU;                       // unit within the block
+
+  const uint16_t d16 = A.dscr[r * A.nb + b];
+  const float d = f16_bits_to_f32(d16);
+
+  float x[8], a[8];
+  load8(A.w, A.dtype, r * A.cols + cg * 8, x);
+  if (A.imp) {
+    const float *ap = A.imp + e * A.cols + cg * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = ap[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = 1.0f;
+  }
+  GroupState<F> S;
+  S.init(x, a);
+  const float *gt = A.gtab + e * A.gtab_e_stride + cg * A.gtab_cg_stride;  // [NG][N]
+
+  // ---- slot scales -------------------------------------------------------
+  float sc[G::IQ1 ? 8 : 16];
+  int fixed_c = 0;
+  if (FIXED) {
+    int c = A.choices[(r * A.nb + b) * G::UNITS + unit];
+    fixed_c = c < G::NC ? c : G::NC - 1;  // out-of-range choices only occur in zeroed blocks
+  }
+  if (!G::IQ1) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) sc[c] = d * (static_cast<float>(2 * c + 1) * 0.125f);
+  } else {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) sc[l] = d * static_cast<float>(2 * l + 1);
+  }
+  // per-lane fixed slot parameters
+  float fs = 0.0f;        // fixed: local scale
+  int fh = 0;             // fixed IQ1_S: shift
+  if (FIXED) {
+    if (!G::IQ1) fs = d * (static_cast<float>(2 * fixed_c + 1) * 0.125f);
+    else fs = d * static_cast<float>(2 * (fixed_c & 7) + 1);
+    fh = (F == IQ1_S) ? (fixed_c >> 3) : 0;
+  }
+  const float fdelta = fh ? -0.125f : 0.125f;
+
+  // ---- sweep -------------------------------------------------------------
+  float best[NSLOT];
+  int bidx[NSLOT];
+#pragma unroll
+  for (int s = 0; s < NSLOT; ++s) { best[s] = __builtin_inff(); bidx[s] = 0; }
+
+  for (int ch = 0; ch < NCH; ++ch) {
+    float cm[NSLOT];
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) cm[s] = __builtin_inff();
+#pragma unroll
+    for (int i = 0; i < CH; i += 2) {
+      const int k = ch * CH + i;
+      float t0[NSLOT], t1[NSLOT];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float *t = p ? t1 : t0;
+        const float *gp = A.grid + static_cast<int64_t>(k + p) * 8;
+        float g[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) g[j] = gp[j];
+        const float q2 = S.term(g);
+        if (!G::IQ1) {
+          const float Gk = gt[k + p];
+          if (FIXED) {
+            t[0] = __builtin_fmaf(fs, Gk, q2);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) t[c] = __builtin_fmaf(sc[c], Gk, q2);
+          }
+        } else {
+          const float G0 = gt[k + p], G1 = gt[N + k + p];
+          const float p0 = __builtin_fmaf(0.125f, S.S2, q2);
+          const float p1 = __builtin_fmaf(-0.125f, S.S2, q2);
+          if (FIXED) {
+            if (F == IQ1_M) {
+              t[0] = __builtin_fmaf(fs, G0, p0);
+              t[1] = __builtin_fmaf(fs, G1, p1);
+            } else {
+              const float pf = __builtin_fmaf(fdelta, S.S2, q2);
+              t[0] = __builtin_fmaf(fs, fh ? G1 : G0, pf);
+            }
+          } else {
+#pragma unroll
+            for (int l = 0; l < 8; ++l) {
+              t[l] = __builtin_fmaf(sc[l], G0, p0);
+              t[8 + l] = __builtin_fmaf(sc[l], G1, p1);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NSLOT; ++s) cm[s] = fminf(fminf(cm[s], t0[s]), t1[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      const bool upd = cm[s] < best[s];
+      best[s] = upd ? cm[s] : best[s];
+      bidx[s] = upd ? ch : bidx[s];
+    }
+  }
+
+  // ---- choice per unit ---------------------------------------------------
+  int cu = 0;     // unit choice (IQ1_S: (h << 3) | ls)
+  int slot = 0;   // slot of this lane's group under that choice
+  if (FIXED) {
+    cu = fixed_c;
+    slot = (F == IQ1_M) ? (best[1] < best[0] ? 1 : 0) : 0;
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) s_best[wave][s][lane] = best[s];
+    __syncthreads();
+    float bs = 0.0f;
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+      float score = 0.0f;
+#pragma unroll
+      for (int i = 0; i < GPU; ++i) {
+        const int w = uw * GPU + i;
+        float bb, s;
+        if (F == IQ1_M) {
+          const float b0 = s_best[w][c][lane], b1 = s_best[w][8 + c][lane];
+          bb = (b1 < b0) ? b1 : b0;          // tie: the lower shift
+          s = sc[c];
+        } else if (F == IQ1_S) {
+          bb = s_best[w][c][lane];
+          s = sc[c & 7];
+        } else {
+          bb = s_best[w][c][lane];
+          s = sc[c];
+        }
+        const float ev = s * bb;
+        score = (i == 0) ? ev : score + ev;
+      }
+      if (c == 0 || score < bs) { bs = score; cu = c; }
+    }
+    if (F == IQ1_M) {
+      float b0 = best[0], b1 = best[8];
+#pragma unroll
+      for (int c = 1; c < 8; ++c) {
+        b0 = (cu == c) ? best[c] : b0;
+        b1 = (cu == c) ? best[8 + c] : b1;
+      }
+      slot = (b1 < b0) ? 8 + cu : cu;
+    } else {
+      slot = cu;
+    }
+  }
+
+  // ---- rescan the chosen chunk for the exact entry ----------------------
+  int chs = bidx[0];
+  float ssel;
+  int hsel;
+  if (FIXED) {
+#pragma unroll
+    for (int s = 1; s < NSLOT; ++s) chs = (slot == s) ? bidx[s] : chs;
+    ssel = fs;
+    hsel = (F == IQ1_M) ? slot : fh;
+  } else {
+#pragma unroll
+    for (int s = 1; s < NSLOT; ++s) chs = (slot == s) ? bidx[s] : chs;
+    ssel = sc[0];
+    if (!G::IQ1) {
+#pragma unroll
+      for (int c = 1; c < 16; ++c) ssel = (slot == c) ? sc[c] : ssel;
+    } else {
+#pragma unroll
+      for (int l = 1; l < 8; ++l) ssel = ((slot & 7) == l) ? sc[l] : ssel;
+    }
+    hsel = G::IQ1 ? (slot >> 3) : 0;
+  }
+  const float dsel = hsel ? -0.125f : 0.125f;
+  float bt = __builtin_inff();
+  int kb = chs * CH;
+  for (int i = 0; i < CH; ++i) {
+    const int k = chs * CH + i;
+    float g[8];
+    load_entry(A.grid + static_cast<int64_t>(k) * 8, g);
+    const float q2 = S.term(g);
+    float t;
+    if (!G::IQ1) {
+      t = __builtin_fmaf(ssel, gt[k], q2);
+    } else {
+      const float pn = __builtin_fmaf(dsel, S.S2, q2);
+      t = __builtin_fmaf(ssel, gt[hsel * N + k], pn);
+    }
+    if (t < bt) { bt = t; kb = k; }
+  }
+  uint32_t mfield;
+  if (!G::IQ1) {
+    uint32_t mask = S.neg;
+    if (S.odd) {
+      float g[8];
+      load_entry(A.grid + static_cast<int64_t>(kb) * 8, g);
+      mask ^= 1u << S.flip_index(g);
+    }
+    mfield = mask;
+  } else {
+    mfield = static_cast<uint32_t>(hsel);
+  }
+  if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
+
+  // ---- pack ----------------------------------------------------------------
+  s_k[wave][lane] = static_cast<uint16_t>(kb);
+  s_m[wave][lane] = static_cast<uint8_t>(mfield);
+  if (wave % GPU == 0) s_c[uw][lane] = static_cast<uint8_t>(cu);
+  __syncthreads();
+  if (wave != 0 || !valid) return;
+  uint8_t *blk = A.out + (r * A.nb + b) * G::BYTES;
+  if (F == IQ2_XXS) {  // sub-block sb: 4 index bytes, then (4 x 7-bit sign index | scale << 28)
+    uint8_t *p = blk + 2 + 8 * sb;
+    uint32_t word = static_cast<uint32_t>(s_c[0][lane]) << 28;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      p[l] = static_cast<uint8_t>(s_k[l][lane]);
+      word |= (static_cast<uint32_t>(s_m[l][lane]) & 0x7fu) << (7 * l);
+    }
+    reinterpret_cast<uint16_t *>(p + 4)[0] = static_cast<uint16_t>(word);
+    reinterpret_cast<uint16_t *>(p + 4)[1] = static_cast<uint16_t>(word >> 16);
+  } else if (F == IQ2_XS) {  // 4 x (9-bit index | 7-bit sign index << 9), scale byte
+#pragma unroll
+    for (int l = 0; l < 4; ++l)
+      reinterpret_cast<uint16_t *>(blk + 2 + 2 * (4 * sb + l))[0] =
+          static_cast<uint16_t>(s_k[l][lane] | ((s_m[l][lane] & 0x7fu) << 9));
+    blk[66 + sb] = static_cast<uint8_t>(s_c[0][lane] | (s_c[1][lane] << 4));
+  } else if (F == IQ2_S) {  // low index bytes, sign masks, high index bits, scale byte
+    uint32_t hi = 0;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      blk[2 + 4 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
+      blk[34 + 4 * sb + l] = s_m[l][lane];
+      hi |= ((s_k[l][lane] >> 8) & 3u) << (2 * l);
+    }
+    blk[66 + sb] = static_cast<uint8_t>(hi);
+    blk[74 + sb] = static_cast<uint8_t>(s_c[0][lane] | (s_c[1][lane] << 4));
+  } else if (F == IQ1_S) {  // low index bytes, (4 x 3 high bits | scale << 12 | shift << 15)
+    const uint32_t c = s_c[0][lane];
+    uint32_t w = ((c & 7u) << 12) | ((c >> 3) << 15);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      blk[2 + 4 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
+      w |= ((s_k[l][lane] >> 8) & 7u) << (3 * l);
+    }
+    reinterpret_cast<uint16_t *>(blk + 34 + 2 * sb)[0] = static_cast<uint16_t>(w);
+  } else {  // IQ1_M, 8 groups: low index bytes, qh nibbles, scale word with d nibble sb
+#pragma unroll
+    for (int l = 0; l < 8; ++l) blk[8 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint32_t lo = ((s_k[2 * qq][lane] >> 8) & 7u) | (static_cast<uint32_t>(s_m[2 * qq][lane]) << 3);
+      const uint32_t hi = ((s_k[2 * qq + 1][lane] >> 8) & 7u) | (static_cast<uint32_t>(s_m[2 * qq + 1][lane]) << 3);
+      blk[32 + 4 * sb + qq] = static_cast<uint8_t>(lo | (hi << 4));
+    }
+    uint32_t w = ((static_cast<uint32_t>(d16) >> (4 * sb)) & 0xfu) << 12;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w |= (s_c[u][lane] & 7u) << (3 * u);
+    reinterpret_cast<uint16_t *>(blk + 48 + 2 * sb)[0] = static_cast<uint16_t>(w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one thread per group.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ld16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
+
+template <int F>
+__global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__ packed, int64_t ngroups,
+                                                      const float *__restrict__ grid, void *out, int dtype) {
+  using G = Geo<F>;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= ngroups) return;
+  const int64_t blkno = i >> 5;
+  const int g = static_cast<int>(i & 31);
+  const uint8_t *blk = packed + blkno * G::BYTES;
+  uint32_t d16, k, mask = 0, h = 0, ls;
+  const int u = g / G::GPU;
+  if (F == IQ2_XXS) {
+    d16 = ld16(blk);
+    const int ib = g >> 2, l = g & 3;
+    const uint32_t word = ld16(blk + 2 + 8 * ib + 4) | (ld16(blk + 2 + 8 * ib + 6) << 16);
+    k = blk[2 + 8 * ib + l];
+    const uint32_t si = (word >> (7 * l)) & 0x7fu;
+    mask = si | ((__builtin_popcount(si) & 1u) << 7);
+    ls = word >> 28;
+  } else if (F == IQ2_XS) {
+    d16 = ld16(blk);
+    const uint32_t v = ld16(blk + 2 + 2 * g);
+    k = v & 511u;
+    const uint32_t si = v >> 9;
+    mask = si | ((__builtin_popcount(si) & 1u) << 7);
+    const uint32_t sbyte = blk[66 + (u >> 1)];
+    ls = (u & 1) ? (sbyte >> 4) : (sbyte & 15u);
+  } else if (F == IQ2_S) {
+    d16 = ld16(blk);
+    k = blk[2 + g] | (((blk[66 + (g >> 2)] >> (2 * (g & 3))) & 3u) << 8);
+    mask = blk[34 + g];
+    const uint32_t sbyte = blk[74 + (u >> 1)];
+    ls = (u & 1) ? (sbyte >> 4) : (sbyte & 15u);
+  } else if (F == IQ1_S) {
+    d16 = ld16(blk);
+    const uint32_t w = ld16(blk + 34 + 2 * (g >> 2));
+    k = blk[2 + g] | (((w >> (3 * (g & 3))) & 7u) << 8);
+    ls = (w >> 12) & 7u;
+    h = w >> 15;
+  } else {
+    d16 = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) d16 |= (ld16(blk + 48 + 2 * w) >> 12) << (4 * w);
+    const uint32_t nb = blk[32 + (g >> 1)];
+    const uint32_t nib = (g & 1) ? (nb >> 4) : (nb & 15u);
+    k = blk[g] | ((nib & 7u) << 8);
+    h = nib >> 3;
+    ls = (ld16(blk + 48 + 2 * (u >> 2)) >> (3 * (u & 3))) & 7u;
+  }
+  const float d = f16_bits_to_f32(static_cast<uint16_t>(d16));
+  float gv[8], y[8];
+  load_entry(grid + static_cast<int64_t>(k) * 8, gv);
+  if (!G::IQ1) {
+    const float s = d * (static_cast<float>(2 * ls + 1) * 0.125f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = s * gv[j];
+      y[j] = ((mask >> j) & 1u) ? -v : v;
+    }
+  } else {
+    const float s = d * static_cast<float>(2 * ls + 1);
+    const float delta = h ? -0.125f : 0.125f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = s * (gv[j] + delta);
+  }
+  if (dtype == 1) {
+    uint4 o;
+    o.x = f32_to_bf16(y[0]) | (static_cast<uint32_t>(f32_to_bf16(y[1])) << 16);
+    o.y = f32_to_bf16(y[2]) | (static_cast<uint32_t>(f32_to_bf16(y[3])) << 16);
+    o.z = f32_to_bf16(y[4]) | (static_cast<uint32_t>(f32_to_bf16(y[5])) << 16);
+    o.w = f32_to_bf16(y[6]) | (static_cast<uint32_t>(f32_to_bf16(y[7])) << 16);
+    reinterpret_cast<uint4 *>(out)[i] = o;
+  } else {
+    float4 *o = reinterpret_cast<float4 *>(out) + 2 * i;
+    o[0] = make_float4(y[0], y[1], y[2], y[3]);
+    o[1] = make_float4(y[4], y[5], y[6], y[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+template <int F>
+static int launch_quantize_t(EncArgs A, hipStream_t stream) {
+  using G = Geo<F>;
+  const int64_t nblocks = A.rows * A.nb;
+  if (nblocks == 0) return 0;
+  const int64_t cgs = A.cols / 8;
+  const int64_t ntab = A.imp ? A.E * cgs : 1;
+  const int NG = G::IQ1 ? 2 : 1;
+  const size_t gbytes = static_cast<size_t>(ntab) * NG * G::N * sizeof(float);
+  const size_t dbytes = static_cast<size_t>(nblocks) * sizeof(uint16_t);
+  void *scratch = nullptr;
+  if (hipMallocAsync(&scratch, gbytes + dbytes + 256, stream) != hipSuccess) return -1;
+  A.gtab = static_cast<float *>(scratch);
+  A.dscr = reinterpret_cast<uint16_t *>(static_cast<char *>(scratch) + ((gbytes + 255) & ~size_t(255)));
+  A.gtab_e_stride = A.imp ? cgs * NG * G::N : 0;
+  A.gtab_cg_stride = A.imp ? NG * G::N : 0;
+
+  const int64_t gthreads = ntab * G::N;
+  hipLaunchKernelGGL(gterm_kernel<F>, dim3(static_cast<unsigned>((gthreads + 255) / 256)), dim3(256), 0, stream,
+                     A.grid, A.imp, A.cols, ntab, A.gtab);
+  hipLaunchKernelGGL(anchor_kernel<F>, dim3(static_cast<unsigned>((nblocks + 255) / 256)), dim3(256), 0, stream, A);
+  A.tiles_per_e = (A.rpe + 63) / 64;
+  A.total_wg = A.E * A.tiles_per_e * A.nb * (32 / G::WGG);
+  if (A.choices)
+    hipLaunchKernelGGL((search_kernel<F, true>), dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::WGG), 0,
+                       stream, A);
+  else
+    hipLaunchKernelGGL((search_kernel<F, false>), dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::WGG), 0,
+                       stream, A);
+  const hipError_t le = hipGetLastError();
+  hipFreeAsync(scratch, stream);
+  return le == hipSuccess ? 0 : -1;
+}
+
+int launch_quantize(int fmt, EncArgs A, hipStream_t stream) {
+  switch (fmt) {
+    case IQ2_XXS: return launch_quantize_t<IQ2_XXS>(A, stream);
+    case IQ2_XS: return launch_quantize_t<IQ2_XS>(A, stream);
+    case IQ2_S: return launch_quantize_t<IQ2_S>(A, stream);
+    case IQ1_S: return launch_quantize_t<IQ1_S>(A, stream);
+    case IQ1_M: return launch_quantize_t<IQ1_M>(A, stream);
+  }
+  return -1;
+}
+
+template <int F>
+static int launch_decode_t(const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
+                           int dtype, hipStream_t stream) {
+  const int64_t ng = rows * (cols / 256) * 32;
+  if (ng == 0) return 0;
+  hipLaunchKernelGGL(decode_kernel<F>, dim3(static_cast<unsigned>((ng + 255) / 256)), dim3(256), 0, stream,
+                     packed, ng, grid, out, dtype);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
+                  int dtype, hipStream_t stream) {
+  switch (fmt) {
+    case IQ2_XXS: return launch_decode_t<IQ2_XXS>(packed, rows, cols, grid, out, dtype, stream);
+    case IQ2_XS: return launch_decode_t<IQ2_XS>(packed, rows, cols, grid, out, dtype, stream);
+    case IQ2_S: return launch_decode_t<IQ2_S>(packed, rows, cols, grid, out, dtype, stream);
+    case IQ1_S: return launch_decode_t<IQ1_S>(packed, rows, cols, grid, out, dtype, stream);
+    case IQ1_M: return launch_decode_t<IQ1_M>(packed, rows, cols, grid, out, dtype, stream);
+  }
+  return -1;
+}
+
+}  // namespace iq

@@ -1,0 +1,35 @@
+// iq_internal.hpp -- argument block and launcher declarations shared by the
+// libiq translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iq {
+
+struct EncArgs {
+  const void *w;
+  int dtype;
+  int64_t rows, cols, rpe, E;
+  int nb;                  // blocks per row (cols / 256)
+  const float *grid;
+  const float *imp;        // [E, cols] or null (flat)
+  const uint8_t *choices;  // [rows, nb, units] or null
+  uint8_t *out;
+  int32_t *status;
+  // filled by the launcher
+  float *gtab;             // weighted norms [tables][NG][N]
+  int64_t gtab_e_stride, gtab_cg_stride;
+  uint16_t *dscr;          // fp16 scale bits per block
+  int64_t tiles_per_e, total_wg;
+};
+
+int launch_quantize(int fmt, EncArgs A, hipStream_t stream);
+int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
+                  int dtype, hipStream_t stream);
+int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
+                   int chunk_rows, float *sums, int64_t *counts, int32_t *status, hipStream_t stream);
+int launch_importance(const float *sums, const int64_t *counts, int E, int64_t K, float floor_rel,
+                      float *imp, int32_t *status, hipStream_t stream);
+
+}  // namespace iq

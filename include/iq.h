@@ -1,0 +1,174 @@
+/*
+ * iq.h -- C ABI of libiq.so: importance-weighted GGML IQ codebook encoding
+ * (IQ2_XXS, IQ2_XS, IQ2_S, IQ1_S, IQ1_M) and imatrix collection on one
+ * MI355X (gfx950).
+ *
+ * Conventions for every entry point
+ *  - Pointers marked (device) must point to device memory of the current HIP
+ *    device; (host) pointers to host memory.  The caller owns every buffer.
+ *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *    a return of IQ_OK means "validated and enqueued", not "finished".
+ *  - A negative return is a host-detected error: nothing was enqueued and no
+ *    output was touched.
+ *  - Problems only the device can see (non-finite data, out-of-range fixed
+ *    choices or expert ids, fp16 overflow of a block scale) are OR-ed into
+ *    *status (device, int32, optional) as IQ_STATUS_* bits; the caller reads it
+ *    after synchronising.  The library never synchronises the stream itself.
+ *  - Dense tensors are row-major and contiguous.  Sizes are in elements.
+ *  - Calls may allocate stream-ordered scratch (hipMallocAsync/hipFreeAsync on
+ *    `stream`); IQ_ERR_HIP reports a failed allocation or launch.
+ *
+ * Sources are cited by page title and section:
+ *  [2735]     "Add imatrix calibration for the GGML formats and use it for fused
+ *             MoE experts" (ModelOpt PR), description.
+ *  [2513]     ModelOpt PR #2513: IQ2_XXS / IQ2_S / IQ1_M commit messages, IQ1_M body.
+ *  [3157]     "[1/5] Let the GGML IQ encoders take fixed per-group choices"
+ *             (ModelOpt PR), description and review.
+ *  [recipes]  modelopt_recipes folder page, IQ1_M CUDA encoder commit.
+ *  [coverage] "MoE expert coverage in imatrix calibration", Facts.
+ */
+#ifndef IQ_H
+#define IQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The five layouts ([2513] commit messages: IQ2_XXS 2.0625 bits/weight,
+ * IQ2_S 2.5625, IQ1_M 1.75, IQ1_S 1.75 - 0.1875; IQ2_XS 9-bit index + 7-bit
+ * sign index per 8 values and a 4-bit scale per 16). */
+typedef enum {
+  IQ_FMT_IQ2_XXS = 0, /* 66-byte blocks, 256-entry grid           */
+  IQ_FMT_IQ2_XS = 1,  /* 74-byte blocks, 512-entry grid           */
+  IQ_FMT_IQ2_S = 2,   /* 82-byte blocks, 1024-entry grid          */
+  IQ_FMT_IQ1_S = 3,   /* 50-byte blocks, 2048-entry signed grid   */
+  IQ_FMT_IQ1_M = 4    /* 56-byte blocks, same 2048-entry grid     */
+} iq_fmt;
+
+typedef enum { IQ_DTYPE_F32 = 0, IQ_DTYPE_BF16 = 1 } iq_dtype;
+
+/* Return codes (host-detected; nothing enqueued). */
+#define IQ_OK 0
+#define IQ_ERR_FMT (-1)    /* unknown format                                  */
+#define IQ_ERR_DTYPE (-2)  /* unknown dtype                                   */
+#define IQ_ERR_NULL (-3)   /* a required pointer is NULL                      */
+#define IQ_ERR_SHAPE (-4)  /* cols % 256 != 0, rows % rows_per_expert != 0, ... */
+#define IQ_ERR_ARG (-5)    /* other invalid argument (top_k, chunk_rows, ...)   */
+#define IQ_ERR_HIP (-6)    /* HIP allocation or launch failure                */
+
+/* Device status bits, OR-ed into *status. */
+#define IQ_STATUS_NONFINITE 1  /* non-finite weight (block encoded as zeros) or activation */
+#define IQ_STATUS_OVERFLOW 2   /* fp16 block scale overflowed (block encoded as zeros)    */
+#define IQ_STATUS_BADCHOICE 4  /* fixed choice >= num_choices (block encoded as zeros)    */
+#define IQ_STATUS_BADIMP 8     /* importance non-finite or negative (block zeros / expert flat) */
+#define IQ_STATUS_BADID 16     /* routed expert id outside [0, num_experts) (pair skipped) */
+
+/* Geometry of one layout ([3157]: each format records choice_groups and
+ * num_choices). */
+typedef struct {
+  int32_t block_values;      /* 256 values per block ([2735] "Checked up front")   */
+  int32_t block_bytes;       /* 66 / 74 / 82 / 50 / 56                             */
+  int32_t grid_size;         /* codebook entries, each 8 floats                    */
+  int32_t choice_groups;     /* choice units per block: 8 / 16 / 16 / 8 / 16       */
+  int32_t num_choices;       /* choices per unit: 16 / 16 / 16 / 16 / 8            */
+  int32_t groups_per_choice; /* 8-value groups sharing one choice: 4 / 2 / 2 / 4 / 2 */
+} iq_format_info_t;
+
+/* Fill *out (host) with the geometry of `fmt`.  Returns IQ_OK or IQ_ERR_FMT /
+ * IQ_ERR_NULL. */
+int iq_format_info(int fmt, iq_format_info_t *out);
+
+/* imatrix collection ([2735] "What imatrix does": per input column the second
+ * moment E[x_j^2]; "Bounded memory": rows are squared 1,024 at a time;
+ * [coverage] Facts: a token's squares are added only to the experts in its
+ * top-k, with one counts entry per expert).
+ *
+ *  x        (device) [T, K] activations, dtype f32 or bf16.
+ *  ids      (device) [T, top_k] int32 routed expert ids, or NULL for a dense
+ *           weight (then num_experts must be 1 and top_k is ignored).
+ *  chunk_rows  rows reduced per chunk (1024 in [2735]); partial sums of each
+ *           chunk are added to `sums` in chunk order, so results do not depend
+ *           on the launch and repeat bit for bit.
+ *  sums     (device) [num_experts, K] f32, ACCUMULATED: sums[e][j] += sum over
+ *           the (t, s) pairs with ids[t][s] == e of x[t][j]^2 (a duplicate id in
+ *           one token counts per occurrence).
+ *  counts   (device) [num_experts] int64, ACCUMULATED: counts[e] += number of
+ *           such pairs (dense: += T).
+ *  status   (device, nullable): IQ_STATUS_NONFINITE when a row that reached an
+ *           expert holds a non-finite value (only touched experts are checked);
+ *           IQ_STATUS_BADID for ids outside [0, num_experts) (those pairs skip).
+ * Errors: IQ_ERR_NULL (x, sums, counts), IQ_ERR_DTYPE, IQ_ERR_ARG (T < 0,
+ * K <= 0, top_k < 1 with ids, num_experts < 1, chunk_rows < 1). */
+int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids,
+                       int top_k, int num_experts, int chunk_rows, float *sums, int64_t *counts,
+                       int32_t *status, hipStream_t stream);
+
+/* Importance from collected statistics ([2735] "What imatrix does" and "Why
+ * the square root": the search weight is sqrt(E[x_j^2]), floored ("Shared
+ * floor"); [coverage] Facts: counts[e] == 0 gives weight 1 on every channel).
+ *
+ *  importance[e][j] = sqrt(max(m_j, floor_rel * mean_j m_j)), m_j = sums[e][j] /
+ *  counts[e] (fp32, IEEE division and square root).  The mean is the exact
+ *  fixed-point sum defined in iq_imatrix_importance's kernel comment, so it is
+ *  reproducible bit for bit.  Experts with counts 0, an all-zero statistic, or
+ *  a non-finite / negative m_j (IQ_STATUS_BADIMP) get all ones.
+ *  sums (device) [E, K] f32; counts (device) [E] int64; importance (device)
+ *  [E, K] f32 (may alias nothing).  floor_rel: 1e-6 is the default used here.
+ * Errors: IQ_ERR_NULL, IQ_ERR_ARG (E < 1, K <= 0, floor_rel < 0 or not finite). */
+int iq_imatrix_importance(const float *sums, const int64_t *counts, int num_experts, int64_t K,
+                          float floor_rel, float *importance, int32_t *status, hipStream_t stream);
+
+/* Importance-weighted IQ encode ([2513] commit messages: fixed anchored fp16
+ * super-block scale, single-pass grid search, IQ2_XXS/XS even-parity sign
+ * index with the weakest element flipped, IQ2_S full sign mask, IQ1 +-1/8
+ * delta with lower-shift-then-lower-entry ties; [3157]: one choice per unit
+ * by least importance-weighted squared error, or fixed by the caller, in
+ * which case only the entry search runs).
+ *
+ *  w           (device) [rows, cols] weight, f32 or bf16; cols % 256 == 0.
+ *  rows_per_expert  rows sharing one importance row: row r uses importance row
+ *              r / rows_per_expert ([coverage] Facts: the slice for each
+ *              expert is applied separately, chunks never cross experts).
+ *              Pass rows for a dense weight.  rows % rows_per_expert == 0.
+ *  grid        (device) [grid_size, 8] f32 codebook (IQ2: magnitudes; IQ1:
+ *              signed values).
+ *  importance  (device) [rows / rows_per_expert, cols] f32 search weights
+ *              a_j, or NULL for the plain (flat, a_j = 1) search.  Use
+ *              iq_imatrix_importance to build it; a row of ones is the flat
+ *              search for an idle expert ([2735] "Idle experts").
+ *  choices     (device) [rows, cols/256, choice_groups] uint8 fixed choices,
+ *              or NULL to search them.  IQ2: local scale in [0,16); IQ1_S:
+ *              (delta_sign << 3) | local scale; IQ1_M: local scale in [0,8).
+ *  out         (device) [rows, cols/256, block_bytes] uint8 payload.
+ *  status      (device, nullable) IQ_STATUS_* bits.
+ * Every block is written; a block holding a non-finite value, a bad
+ * importance value, an out-of-range choice, an fp16-overflowing scale, or only
+ * zeros is written as all-zero bytes ([3157] review: all-zero block -> all-zero
+ * payload).
+ * Errors: IQ_ERR_FMT, IQ_ERR_DTYPE, IQ_ERR_NULL (w, grid, out), IQ_ERR_SHAPE
+ * (rows < 0, cols <= 0 or % 256, rows_per_expert < 1 or not dividing rows),
+ * IQ_ERR_HIP. */
+int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
+                int64_t rows_per_expert, const float *grid, const float *importance,
+                const uint8_t *choices, uint8_t *out, int32_t *status, hipStream_t stream);
+
+/* Decode ([2513]: dequantize_row semantics; IQ1_M d reassembled from the top
+ * nibbles of the four scale words, one 3-bit scale per two groups).
+ *  packed (device) [rows, cols/256, block_bytes]; grid (device) [grid_size, 8];
+ *  out (device) [rows, cols] f32 or bf16 (bf16: round to nearest even).
+ *  IQ2: out = +-(s * g), s = d * (2 ls + 1) / 8.  IQ1: out = s * (g +- 1/8),
+ *  s = d * (2 ls + 1).
+ * Errors: IQ_ERR_FMT, IQ_ERR_DTYPE, IQ_ERR_NULL, IQ_ERR_SHAPE. */
+int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid,
+                  void *out, int dtype, hipStream_t stream);
+
+/* Short text for a return code (static storage). */
+const char *iq_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IQ_H */

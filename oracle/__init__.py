@@ -52,6 +52,8 @@ def lib():
         L.orc_f16_to_f32.restype = ctypes.c_float
         L.orc_collect.argtypes = [P, i64, i64, P, ci, ci, P, P]
         L.orc_importance.argtypes = [P, P, ci, i64, ctypes.c_float, P]
+        L.orc_fixed_mean.argtypes = [P, i64]
+        L.orc_fixed_mean.restype = ctypes.c_float
         L.orc_anchor.argtypes = [ci, P, P]
         L.orc_anchor.restype = ctypes.c_uint16
         L.orc_encode_block.argtypes = [ci, P, P, P, ci, P, ci, P]
@@ -116,6 +118,11 @@ def importance(sums32, counts, floor_rel: float = 1e-6):
     out = np.empty((E, K), dtype=np.float32)
     st = lib().orc_importance(_p(s), _p(c), E, K, float(floor_rel), _p(out))
     return out, st
+
+
+def fixed_mean(m):
+    m = _f32(m).ravel()
+    return float(lib().orc_fixed_mean(_p(m), m.size))
 
 
 def anchor(fmt, block):

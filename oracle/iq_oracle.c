@@ -36,8 +36,8 @@
  *  R5  amax == 0, fp16(d) == 0, non-finite inputs, fp16 overflow and
  *      out-of-range fixed choices give an all-zero block (the all-zero rule of
  *      the [3157] review); the last three also raise a status bit.
- *  R6  imatrix floor: a_j = sqrt(max(E_j, 1e-6 * mean_j E_j)); mean over the
- *      fp32 E_j, summed in fp64 in ascending j.
+ *  R6  imatrix floor: a_j = sqrt(max(E_j, 1e-6 * mean_j E_j)); the mean is an
+ *      exact fixed-point sum (orc_fixed_mean) so every summation order agrees.
  *  R7  odd sign parity (IQ2_XXS, IQ2_XS): per candidate entry, flip the element
  *      with the least a_j*|x_j|*g_kj (lowest j on ties).
  *  R8  x = -0 counts as positive.
@@ -163,7 +163,31 @@ int orc_collect(const float *x, int64_t T, int64_t K, const int32_t *ids, int to
 
 /* Importance a_j = sqrt(floored E[x_j^2]) per expert  ([2735] "What imatrix
  * does", "Why the square root", "Shared floor"; [coverage] Facts: count 0 ->
- * weight 1 on every channel).  sums are the fp32 statistics.  R6. */
+ * weight 1 on every channel).  sums are the fp32 statistics.  R6.
+ *
+ * The floor is floor_rel times the mean of the m_j.  So that any summation
+ * order gives the same bits, the mean is defined through an exact fixed-point
+ * sum: with M = max_j m_j = f * 2^e (f in [0.5, 1)) and L = ceil(log2 K),
+ * s = 62 - e - L, total = sum_j floor(m_j * 2^s) (an exact integer below 2^62),
+ * mean = fp32( fp64(total) * 2^-s / K ). */
+static int ceil_log2(int64_t K) {
+  int L = 0;
+  while (((int64_t)1 << L) < K) ++L;
+  return L;
+}
+
+float orc_fixed_mean(const float *m, int64_t K) {
+  float M = 0.0f;
+  for (int64_t j = 0; j < K; ++j) M = fmaxf(M, m[j]);
+  if (M == 0.0f) return 0.0f;
+  int e;
+  frexp((double)M, &e);
+  int s = 62 - e - ceil_log2(K);
+  uint64_t total = 0;
+  for (int64_t j = 0; j < K; ++j) total += (uint64_t)floor(ldexp((double)m[j], s));
+  return (float)(ldexp((double)total, -s) / (double)K);
+}
+
 int orc_importance(const float *sums, const int64_t *counts, int num_experts, int64_t K,
                    float floor_rel, float *imp) {
   int st = 0;
@@ -172,21 +196,18 @@ int orc_importance(const float *sums, const int64_t *counts, int num_experts, in
     const float *se = sums + (int64_t)e * K;
     float *ie = imp + (int64_t)e * K;
     int flat = counts[e] <= 0;
-    double acc = 0.0;
     if (!flat) {
       float c = (float)counts[e];
       for (int64_t j = 0; j < K; ++j) {
         m[j] = se[j] / c;
-        if (!isfinite(m[j]) || m[j] < 0.0f) st |= ORC_ST_BADIMP;
-        acc += (double)m[j];
+        if (!isfinite(m[j]) || m[j] < 0.0f) { st |= ORC_ST_BADIMP; flat = 1; }
       }
-      if (!(acc > 0.0) || !isfinite(acc)) flat = 1; /* nothing usable: flat */
     }
-    if (flat) {
+    float mean = flat ? 0.0f : orc_fixed_mean(m, K);
+    if (flat || mean == 0.0f) { /* idle expert or nothing usable: flat weights */
       for (int64_t j = 0; j < K; ++j) ie[j] = 1.0f;
       continue;
     }
-    float mean = (float)(acc / (double)K);
     float fl = floor_rel * mean;
     for (int64_t j = 0; j < K; ++j) ie[j] = sqrtf(fmaxf(m[j], fl));
   }

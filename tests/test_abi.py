@@ -1,0 +1,95 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/iq.h declares, its format table agrees with the oracle's independent
+one, and host-side validation rejects bad arguments before anything runs."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iq.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(iq_\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def api():
+    from ggml_iq_codebook_imatrix_amd import api as a
+    if not os.path.exists(a.LIB_PATH):
+        from ggml_iq_codebook_imatrix_amd import build
+        build.build()
+    return a
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["iq_format_info", "iq_imatrix_collect", "iq_imatrix_importance", "iq_quantize", "iq_dequantize",
+         "iq_error_string"])
+
+
+def test_library_exports_every_declared_symbol(api):
+    lib = api.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (iq_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+        assert name in api.SIGNATURES
+
+
+def test_format_table_matches_oracle(api, orc):
+    for fmt in api.FORMATS:
+        info = api.format_info(fmt)
+        geo = orc.geometry(fmt)
+        assert info["block_values"] == 256
+        assert info["block_bytes"] == geo["block_bytes"]
+        assert info["grid_size"] == geo["grid_n"]
+        assert info["choice_groups"] == geo["units"]
+        assert info["num_choices"] == geo["num_choices"]
+        assert info["groups_per_choice"] == geo["groups_per_unit"]
+
+
+def test_host_validation_quantize(api):
+    L = api.lib()
+    q = lambda fmt=0, w=FAKE, dt=1, rows=64, cols=512, rpe=64, grid=FAKE, out=FAKE: L.iq_quantize(
+        fmt, w, dt, rows, cols, rpe, grid, None, None, out, None, None)
+    assert q(fmt=5) == -1 and q(fmt=-1) == -1
+    assert q(dt=2) == -2
+    assert q(w=None) == -3 and q(grid=None) == -3 and q(out=None) == -3
+    assert q(cols=300) == -4 and q(cols=0) == -4 and q(rows=-1) == -4
+    assert q(rpe=0) == -4 and q(rpe=48) == -4
+    assert L.iq_format_info(0, None) == -3
+    assert api.lib().iq_error_string(-4) == b"invalid shape"
+
+
+def test_host_validation_collect_importance_decode(api):
+    L = api.lib()
+    c = lambda x=FAKE, dt=1, T=16, K=64, ids=None, top_k=0, E=1, chunk=1024, sums=FAKE, counts=FAKE: \
+        L.iq_imatrix_collect(x, dt, T, K, ids, top_k, E, chunk, sums, counts, None, None)
+    assert c(dt=7) == -2
+    assert c(x=None) == -3 and c(sums=None) == -3 and c(counts=None) == -3
+    assert c(T=-1) == -5 and c(K=0) == -5 and c(chunk=0) == -5 and c(E=0) == -5
+    assert c(E=4) == -5                           # dense needs one statistic
+    assert c(ids=FAKE, top_k=0, E=4) == -5
+    imp = lambda s=FAKE, cnt=FAKE, E=1, K=8, fl=1e-6, out=FAKE: L.iq_imatrix_importance(s, cnt, E, K, fl, out,
+                                                                                       None, None)
+    assert imp(s=None) == -3 and imp(out=None) == -3
+    assert imp(E=0) == -5 and imp(K=0) == -5 and imp(fl=-1.0) == -5 and imp(fl=float("nan")) == -5
+    d = lambda fmt=0, p=FAKE, rows=4, cols=256, grid=FAKE, out=FAKE, dt=0: L.iq_dequantize(
+        fmt, p, rows, cols, grid, out, dt, None)
+    assert d(fmt=9) == -1 and d(dt=3) == -2 and d(p=None) == -3 and d(cols=100) == -4
+
+
+def test_binding_fails_loudly_without_library(api, monkeypatch, tmp_path):
+    monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(api, "_lib", None)
+    with pytest.raises(api.IQError):
+        api.lib()

@@ -175,6 +175,22 @@ def test_collect_flags_nonfinite_and_bad_ids(orc):
 # --------------------------------------------------------------------------
 # Importance: closed form of the floored square root, flat for idle experts
 # --------------------------------------------------------------------------
+def _exact_fixed_mean(m):
+    """The floor's mean from its definition, in Python integers."""
+    from fractions import Fraction
+    import math
+    m = np.asarray(m, np.float32)
+    M = float(m.max())
+    if M == 0:
+        return 0.0
+    e = math.frexp(M)[1]
+    L = max(0, math.ceil(math.log2(m.size)))
+    s = 62 - e - L
+    total = sum(math.floor(Fraction(float(v)) * Fraction(2) ** s) for v in m)
+    assert total < 2 ** 62
+    return float(np.float32(float(total) * 2.0 ** -s / m.size))
+
+
 def test_importance_closed_form(orc):
     g = inputs.rng(9)
     K = 512
@@ -186,14 +202,32 @@ def test_importance_closed_form(orc):
     assert np.all(imp[1] == 1.0)           # count 0 -> weight 1 on every channel
     for e in (0, 2, 3):
         m = (sums[e] / np.float32(counts[e])).astype(np.float32)
-        mean = np.float32(m.astype(np.float64).sum() / K)
-        fl = np.float32(np.float32(1e-6) * mean)
+        mean = _exact_fixed_mean(m)
+        assert orc.fixed_mean(m) == np.float32(mean)
+        # the fixed-point mean is the true mean to fp64 accuracy
+        assert abs(mean - m.astype(np.float64).mean()) <= 1e-6 * mean
+        fl = np.float32(np.float32(1e-6) * np.float32(mean))
         ref = np.sqrt(np.maximum(m, fl)).astype(np.float32)
         assert np.array_equal(imp[e], ref)
-    assert np.all(imp[2, :7] > 0)
+    assert np.all(imp[2, :7] == np.sqrt(np.float32(np.float32(1e-6) * np.float32(
+        _exact_fixed_mean((sums[2] / np.float32(37)).astype(np.float32))))))
     # all-zero statistic with count > 0: nothing usable -> flat
     imp2, _ = orc.importance(np.zeros((1, 8), np.float32), np.array([5]), 1e-6)
     assert np.all(imp2 == 1.0)
+    # non-finite statistic: flagged, expert flat
+    bad = np.ones((1, 8), np.float32)
+    bad[0, 3] = np.inf
+    imp3, st3 = orc.importance(bad, np.array([2]), 1e-6)
+    assert st3 & orc.ST_BADIMP and np.all(imp3 == 1.0)
+
+
+def test_fixed_mean_order_free_and_exact(orc):
+    g = inputs.rng(19)
+    for K in (1, 7, 2048, 5000):
+        m = (g.lognormal(0, 3, K)).astype(np.float32)
+        m[g.random(K) < 0.1] = 0.0
+        assert orc.fixed_mean(m) == np.float32(_exact_fixed_mean(m))
+        assert orc.fixed_mean(g.permutation(m)) == orc.fixed_mean(m)
 
 
 # --------------------------------------------------------------------------
