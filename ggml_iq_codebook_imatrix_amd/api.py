@@ -31,6 +31,7 @@ SIGNATURES = {
     "iq_imatrix_importance": ([_P, _P, _I, _I64, _F, _P, _P, _P], _I),
     "iq_quantize": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
     "iq_dequantize": ([_I, _P, _I64, _I64, _P, _P, _I, _P], _I),
+    "iq_time_next_search": ([_P, _P], _I),
     "iq_error_string": ([_I], ctypes.c_char_p),
 }
 
@@ -183,6 +184,16 @@ def quantize(fmt, w: torch.Tensor, grid: torch.Tensor, importance: torch.Tensor 
         if st:
             raise IQError(f"iq_quantize device status {st:#x}")
     return out
+
+
+def time_next_search(start, stop):
+    """Profiling hook: the next quantize() on this thread records the two
+    torch.cuda.Event objects around its search kernel (events are materialised
+    here by a first record)."""
+    for e in (start, stop):
+        e.record()
+    _check(lib().iq_time_next_search(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)),
+           "iq_time_next_search")
 
 
 def dequantize(fmt, packed: torch.Tensor, grid: torch.Tensor, dtype=torch.float32,

@@ -20,10 +20,20 @@ constexpr FmtRow kFmt[5] = {
     {56, 2048, 16, 8, 2},  // IQ1_M
 };
 
+thread_local hipEvent_t t_search_start = nullptr, t_search_stop = nullptr;
+
 bool bad_fmt(int fmt) { return fmt < 0 || fmt > 4; }
 bool bad_dtype(int dt) { return dt != IQ_DTYPE_F32 && dt != IQ_DTYPE_BF16; }
 
 }  // namespace
+
+namespace iq {
+void take_search_events(hipEvent_t *start, hipEvent_t *stop) {
+  *start = t_search_start;
+  *stop = t_search_stop;
+  t_search_start = t_search_stop = nullptr;
+}
+}  // namespace iq
 
 extern "C" {
 
@@ -100,6 +110,13 @@ int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, co
   if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
   if (rows * (cols / 256) * 32 / 256 >= (int64_t(1) << 31)) return IQ_ERR_SHAPE;
   return iq::launch_decode(fmt, packed, rows, cols, grid, out, dtype, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
+}
+
+int iq_time_next_search(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return IQ_ERR_NULL;
+  t_search_start = start;
+  t_search_stop = stop;
+  return IQ_OK;
 }
 
 const char *iq_error_string(int code) {

@@ -643,6 +643,9 @@ static int launch_quantize_t(EncArgs A, hipStream_t stream) {
   hipLaunchKernelGGL(anchor_kernel<F>, dim3(static_cast<unsigned>((nblocks + 255) / 256)), dim3(256), 0, stream, A);
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb * (32 / G::WGG);
+  hipEvent_t ev0, ev1;
+  take_search_events(&ev0, &ev1);
+  if (ev0) hipEventRecord(ev0, stream);
   if (A.choices)
     hipLaunchKernelGGL((search_kernel<F, true>), dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::WGG), 0,
                        stream, A);
@@ -650,6 +653,7 @@ static int launch_quantize_t(EncArgs A, hipStream_t stream) {
     hipLaunchKernelGGL((search_kernel<F, false>), dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::WGG), 0,
                        stream, A);
   const hipError_t le = hipGetLastError();
+  if (ev1) hipEventRecord(ev1, stream);
   hipFreeAsync(scratch, stream);
   return le == hipSuccess ? 0 : -1;
 }

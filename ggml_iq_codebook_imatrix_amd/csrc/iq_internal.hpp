@@ -24,6 +24,9 @@ struct EncArgs {
   int64_t tiles_per_e, total_wg;
 };
 
+// events registered by iq_time_next_search for this host thread (cleared on take)
+void take_search_events(hipEvent_t *start, hipEvent_t *stop);
+
 int launch_quantize(int fmt, EncArgs A, hipStream_t stream);
 int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
                   int dtype, hipStream_t stream);

@@ -165,6 +165,14 @@ int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
 int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid,
                   void *out, int dtype, hipStream_t stream);
 
+/* Profiling hook (not part of the method): the next iq_quantize call made on
+ * the calling host thread records `start` on its stream just before its search
+ * kernel and `stop` just after it, so hipEventElapsedTime gives that kernel's
+ * duration alone; the hook then clears itself.  Both events must be created
+ * by the caller on the current device, or both NULL to clear.
+ * Errors: IQ_ERR_NULL when exactly one event is NULL. */
+int iq_time_next_search(hipEvent_t start, hipEvent_t stop);
+
 /* Short text for a return code (static storage). */
 const char *iq_error_string(int code);
 

@@ -32,7 +32,7 @@ def api():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["iq_format_info", "iq_imatrix_collect", "iq_imatrix_importance", "iq_quantize", "iq_dequantize",
-         "iq_error_string"])
+         "iq_time_next_search", "iq_error_string"])
 
 
 def test_library_exports_every_declared_symbol(api):
@@ -68,6 +68,8 @@ def test_host_validation_quantize(api):
     assert q(rpe=0) == -4 and q(rpe=48) == -4
     assert L.iq_format_info(0, None) == -3
     assert api.lib().iq_error_string(-4) == b"invalid shape"
+    assert L.iq_time_next_search(FAKE, None) == -3 and L.iq_time_next_search(None, FAKE) == -3
+    assert L.iq_time_next_search(None, None) == 0
 
 
 def test_host_validation_collect_importance_decode(api):
