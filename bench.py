@@ -55,6 +55,8 @@ def main() -> int:
     ap.add_argument("--reps", type=int, default=10, help="repetitions per extra encode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the per-layout / MoE / 17408x5120 tables")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run 3 plain device copies of this many MiB (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the encoder shards by rows or experts "
@@ -69,6 +71,15 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_mb:
+        n = args.copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n}))
+        return 0
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
 
     def to_dev_bf16(a32):

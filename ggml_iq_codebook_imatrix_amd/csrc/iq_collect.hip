@@ -15,7 +15,7 @@
 // Design.  No floating-point atomics: a pass marks, per 1,024-row chunk and
 // expert, which tokens route there (bitmaps built with integer atomics, whose
 // result does not depend on order); a second pass reduces each (chunk, expert,
-// 256-column tile) with 16 waves that each own a fixed slice of the chunk's
+// 128-column tile) with 16 waves that each own a fixed slice of the chunk's
 // rows, combined in wave order; a last pass adds the chunk partials to the
 // running sums in chunk order.  The sums therefore repeat bit for bit, and no
 // x^2 temporary of the activation's size is ever materialised.
@@ -50,105 +50,99 @@ __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__res
 }
 
 // Pass 2: partial[chunk][e][K] = sum over the chunk's rows routed to e of x^2.
-// Workgroup = 16 waves x 64 lanes; lane owns 4 columns of a 256-column tile;
-// wave w owns rows [w * rpw, (w + 1) * rpw) of the chunk.
-template <int DT>
+// Workgroup = 16 waves x 64 lanes over a 128-column tile; lane owns 2 columns;
+// wave w owns rows [w * rpw, (w + 1) * rpw) of the chunk and adds them in row
+// order, loading 16 rows per batch; the 16 wave partials are then added in wave
+// order.
+constexpr int kTile = 128, kBatch = 16;
+
+template <int DT, bool PAIR>
 __global__ void __launch_bounds__(1024) collect_partial_kernel(const void *__restrict__ x, int64_t T, int64_t K,
                                                                 const int32_t *__restrict__ ids, int top_k,
                                                                 int E, int chunk_rows, int W,
                                                                 const uint32_t *__restrict__ bm,
                                                                 float *__restrict__ partial, int32_t *status) {
-  __shared__ float s_part[16][256];
-  const int64_t ntile = (K + 255) / 256;
+  __shared__ float s_part[16][kTile];
+  const int64_t ntile = (K + kTile - 1) / kTile;
   const int64_t tile = blockIdx.x % ntile;
   const int64_t ce = blockIdx.x / ntile;  // chunk * E + e
   const int e = static_cast<int>(ce % E);
   const int64_t chunk = ce / E;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: row bookkeeping stays scalar
+  const int lane = threadIdx.x & 63;
   const int64_t t0 = chunk * chunk_rows;
   const int64_t n = (T - t0 < chunk_rows) ? (T - t0) : chunk_rows;
   const int64_t rpw = (((chunk_rows + 15) / 16) + 63) / 64 * 64;  // rows per wave, whole 64-row words
-  const int64_t c0 = tile * 256 + lane * 4;
-  const bool vec = (K & 3) == 0 && c0 + 3 < K;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t cl = tile * kTile + lane * 2;             // this lane's first column
+  // lanes past the last column read a valid column and their results are dropped
+  const int64_t c0 = cl < K ? cl : (PAIR ? K - 2 : K - 1);
+  float acc0 = 0.0f, acc1 = 0.0f;
   bool finite = true;
   for (int64_t base = wave * rpw; base < (wave + 1) * rpw && base < n; base += 64) {
-    // 64 positions starting at base: membership mask (uniform across the wave)
-    uint64_t mm;
     const int64_t cnt = (n - base < 64) ? (n - base) : 64;
     const uint64_t live = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
+    uint64_t mm = live;
     if (ids) {
       const uint32_t *wrow = bm + ce * W;
       const uint64_t lo = wrow[base >> 5];
       const uint64_t hi = ((base >> 5) + 1 < W) ? wrow[(base >> 5) + 1] : 0u;
       mm = (lo | (hi << 32)) & live;
-    } else {
-      mm = live;
     }
     while (mm) {
-      int64_t tok[4];
-      int m[4];
+      // next kBatch member rows in ascending order; empty slots reuse a valid
+      // row and contribute an exact zero, so the loads need no branches
+      int64_t tok[kBatch];
+      bool ok[kBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (mm) {
-          const int bit = __builtin_ctzll(mm);
-          mm &= mm - 1;
-          tok[u] = t0 + base + bit;
-          m[u] = 1;
-        } else {
-          tok[u] = -1;
-          m[u] = 0;
-        }
+      for (int u = 0; u < kBatch; ++u) {
+        ok[u] = mm != 0;
+        tok[u] = t0 + base + (ok[u] ? __builtin_ctzll(mm) : 0);
+        mm &= mm - 1;
       }
-      float v[4][4];
+      float v0[kBatch], v1[kBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[u][c] = 0.0f;
-        if (tok[u] < 0) continue;
+      for (int u = 0; u < kBatch; ++u) {
         const int64_t off = tok[u] * K + c0;
-        if (vec) {
+        if (PAIR) {  // even K: one 2-column load
           if (DT == 1) {
-            const uint2 qv = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + off);
-            v[u][0] = __uint_as_float(qv.x << 16);
-            v[u][1] = __uint_as_float(qv.x & 0xffff0000u);
-            v[u][2] = __uint_as_float(qv.y << 16);
-            v[u][3] = __uint_as_float(qv.y & 0xffff0000u);
+            const uint32_t q = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(x) + off);
+            v0[u] = __uint_as_float(q << 16);
+            v1[u] = __uint_as_float(q & 0xffff0000u);
           } else {
-            const float4 qv = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
-            v[u][0] = qv.x; v[u][1] = qv.y; v[u][2] = qv.z; v[u][3] = qv.w;
+            const float2 q = *reinterpret_cast<const float2 *>(static_cast<const float *>(x) + off);
+            v0[u] = q.x;
+            v1[u] = q.y;
           }
         } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (c0 + c < K)
-              v[u][c] = DT == 1 ? bf16_to_f32(static_cast<const uint16_t *>(x)[off + c])
-                                : static_cast<const float *>(x)[off + c];
-        }
-        if (ids) {  // multiplicity of e in this token's top-k
-          int mult = 0;
-          for (int s = 0; s < top_k; ++s) mult += ids[tok[u] * top_k + s] == e;
-          m[u] = mult;
+          const int64_t o1 = (c0 + 1 < K) ? off + 1 : off;
+          v0[u] = DT == 1 ? bf16_to_f32(static_cast<const uint16_t *>(x)[off]) : static_cast<const float *>(x)[off];
+          v1[u] = DT == 1 ? bf16_to_f32(static_cast<const uint16_t *>(x)[o1]) : static_cast<const float *>(x)[o1];
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        for (int rep = 0; rep < m[u]; ++rep) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            finite = finite && finite_f(v[u][c]);
-            acc[c] = __builtin_fmaf(v[u][c], v[u][c], acc[c]);
-          }
+      for (int u = 0; u < kBatch; ++u) {
+        int mult = ok[u] ? 1 : 0;
+        if (ids && ok[u]) {  // multiplicity of e in this token's top-k (usually 1)
+          mult = 0;
+          for (int s2 = 0; s2 < top_k; ++s2) mult += ids[tok[u] * top_k + s2] == e;
+        }
+        const float a0 = mult ? v0[u] : 0.0f, a1 = mult ? v1[u] : 0.0f;
+        finite = finite && finite_f(a0) && finite_f(a1);
+        acc0 = __builtin_fmaf(a0, a0, acc0);
+        acc1 = __builtin_fmaf(a1, a1, acc1);
+        for (int rep = 1; rep < mult; ++rep) {
+          acc0 = __builtin_fmaf(a0, a0, acc0);
+          acc1 = __builtin_fmaf(a1, a1, acc1);
         }
       }
     }
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) s_part[wave][lane * 4 + c] = acc[c];
+  s_part[wave][lane * 2] = acc0;
+  s_part[wave][lane * 2 + 1] = acc1;
   if (!finite) raise_status(status, ST_NONFINITE);
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int64_t col = tile * 256 + threadIdx.x;
+  if (threadIdx.x < kTile) {  // columns past K (clamped lanes) are not stored
+    const int64_t col = tile * kTile + threadIdx.x;
     float p = s_part[0][threadIdx.x];
 #pragma unroll
     for (int w = 1; w < 16; ++w) p = p + s_part[w][threadIdx.x];
@@ -183,14 +177,21 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   if (ids)
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks)), dim3(256), 0, stream, ids, T,
                        top_k, E, chunk_rows, W, bm, counts, status);
-  const int64_t ntile = (K + 255) / 256;
+  const int64_t ntile = (K + kTile - 1) / kTile;
   const dim3 g2(static_cast<unsigned>(nchunks * E * ntile));
-  if (dtype == 1)
-    hipLaunchKernelGGL(collect_partial_kernel<1>, g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E, chunk_rows,
-                       W, bm, partial, status);
+  const bool pair = (K & 1) == 0;
+  if (dtype == 1 && pair)
+    hipLaunchKernelGGL((collect_partial_kernel<1, true>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
+                       chunk_rows, W, bm, partial, status);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((collect_partial_kernel<1, false>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
+                       chunk_rows, W, bm, partial, status);
+  else if (pair)
+    hipLaunchKernelGGL((collect_partial_kernel<0, true>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
+                       chunk_rows, W, bm, partial, status);
   else
-    hipLaunchKernelGGL(collect_partial_kernel<0>, g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E, chunk_rows,
-                       W, bm, partial, status);
+    hipLaunchKernelGGL((collect_partial_kernel<0, false>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
+                       chunk_rows, W, bm, partial, status);
   hipLaunchKernelGGL(collect_combine_kernel, dim3(static_cast<unsigned>((EK + 255) / 256)), dim3(256), 0, stream,
                      partial, nchunks, EK, sums, counts, ids ? int64_t(0) : T);
   const hipError_t le = hipGetLastError();
@@ -223,13 +224,14 @@ __device__ __forceinline__ int frexp_exponent(float m) {  // m > 0: m = f 2^e, f
   return (32 - __builtin_clz(bits & 0x7fffffu)) - 149;
 }
 
-__global__ void __launch_bounds__(256) importance_kernel(const float *__restrict__ sums,
+__global__ void __launch_bounds__(1024) importance_kernel(const float *__restrict__ sums,
                                                           const int64_t *__restrict__ counts, int64_t K,
                                                           float floor_rel, int L, float *__restrict__ imp,
                                                           int32_t *status) {
-  __shared__ float s_f[4];
-  __shared__ int s_i[4];
-  __shared__ unsigned long long s_u[4];
+  constexpr int NT = 1024, NW = NT / 64;
+  __shared__ float s_f[NW];
+  __shared__ int s_i[NW];
+  __shared__ unsigned long long s_u[NW];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *se = sums + static_cast<int64_t>(e) * K;
@@ -240,7 +242,7 @@ __global__ void __launch_bounds__(256) importance_kernel(const float *__restrict
   int bad = 0;
   if (!flat) {
     const float fc = static_cast<float>(c);
-    for (int64_t j = tid; j < K; j += 256) {
+    for (int64_t j = tid; j < K; j += NT) {
       const float m = se[j] / fc;
       bad |= !(finite_f(m) && m >= 0.0f);
       mx = fmaxf(mx, m);
@@ -252,33 +254,35 @@ __global__ void __launch_bounds__(256) importance_kernel(const float *__restrict
     }
     if (lane == 0) { s_f[wave] = mx; s_i[wave] = bad; }
     __syncthreads();
-    mx = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
-    bad = s_i[0] | s_i[1] | s_i[2] | s_i[3];
+    mx = s_f[0];
+    bad = s_i[0];
+    for (int w = 1; w < NW; ++w) { mx = fmaxf(mx, s_f[w]); bad |= s_i[w]; }
     if (bad && tid == 0) raise_status(status, ST_BADIMP);
     flat = bad || mx == 0.0f;
   }
   if (flat) {
     __syncthreads();
-    for (int64_t j = tid; j < K; j += 256) ie[j] = 1.0f;
+    for (int64_t j = tid; j < K; j += NT) ie[j] = 1.0f;
     return;
   }
   const int s = 62 - frexp_exponent(mx) - L;
   unsigned long long tot = 0;
-  for (int64_t j = tid; j < K; j += 256) tot += fixed_term(ie[j], s);
+  for (int64_t j = tid; j < K; j += NT) tot += fixed_term(ie[j], s);
   for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
   if (lane == 0) s_u[wave] = tot;
   __syncthreads();
-  tot = s_u[0] + s_u[1] + s_u[2] + s_u[3];
+  tot = 0;
+  for (int w = 0; w < NW; ++w) tot += s_u[w];
   const float mean = static_cast<float>(ldexp(static_cast<double>(tot), -s) / static_cast<double>(K));
   const float fl = floor_rel * mean;
-  for (int64_t j = tid; j < K; j += 256) ie[j] = sqrtf(fmaxf(ie[j], fl));
+  for (int64_t j = tid; j < K; j += NT) ie[j] = sqrtf(fmaxf(ie[j], fl));
 }
 
 int launch_importance(const float *sums, const int64_t *counts, int E, int64_t K, float floor_rel, float *imp,
                       int32_t *status, hipStream_t stream) {
   int L = 0;
   while ((int64_t(1) << L) < K) ++L;
-  hipLaunchKernelGGL(importance_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream, sums, counts, K,
+  hipLaunchKernelGGL(importance_kernel, dim3(static_cast<unsigned>(E)), dim3(1024), 0, stream, sums, counts, K,
                      floor_rel, L, imp, status);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

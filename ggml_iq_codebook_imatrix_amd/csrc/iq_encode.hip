@@ -31,9 +31,10 @@
 //
 // gfx950 design.  One wave per 8-value group and 64 rows per wave: the grid
 // entry and the weighted norm G_k are then the same for all 64 lanes, so they
-// arrive as scalar loads (SGPR operands) and cost no VGPRs or LDS bandwidth;
-// G_k is precomputed once per (expert, column group) by gterm_kernel.  The
-// sweep keeps, per slot, a running minimum per 16-entry chunk (v_min3 pairs)
+// arrive as scalar loads and cost no LDS bandwidth; G_k is precomputed once per
+// (expert, column group) by gterm_kernel and copied to a VGPR per entry so the
+// candidate FMAs can co-issue across waves.  The
+// sweep keeps, per slot, a running minimum per 32-entry chunk (v_min3 pairs)
 // and the index of the chunk holding the first minimum; after the unit's
 // choice is known the chosen chunk is rescanned to recover the exact entry.
 // A workgroup holds the groups whose payload bytes nobody else writes (one
@@ -58,30 +59,69 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total) {
 }
 
 // ---------------------------------------------------------------------------
-// Anchor: one thread per block.  Writes the fp16 scale bits (0 = all-zero
+// Importance check: one wave per (expert, block), 4 values per lane;
+// flags[e * nb + b] = 1 when the block's 256 importance values hold a
+// non-finite or negative value.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) impcheck_kernel(const float *__restrict__ imp, int64_t n,
+                                                        uint8_t *__restrict__ flags) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // (e * nb + b)
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  const float4 q = reinterpret_cast<const float4 *>(imp + i * 256)[lane];  // cols = nb * 256
+  const bool ok = finite_f(q.x) && finite_f(q.y) && finite_f(q.z) && finite_f(q.w) && q.x >= 0.0f &&
+                  q.y >= 0.0f && q.z >= 0.0f && q.w >= 0.0f;
+  const uint64_t bad = __ballot(!ok);
+  if (lane == 0) flags[i] = bad ? 1 : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Anchor: 32 lanes per block, 8 contiguous values per lane (coalesced), two
+// blocks per wave.  amax and finiteness reduce across the 32 lanes (exact); the
+// IQ1_M sum of squares is the sequential chain over j = 0..255, run by one lane
+// from an LDS copy of the block.  Writes the fp16 scale bits (0 = all-zero
 // block) to dscr and, for layouts with a leading d field, to the payload.
 // ---------------------------------------------------------------------------
 template <int F>
-__global__ void __launch_bounds__(256) anchor_kernel(EncArgs A) {
+__global__ void __launch_bounds__(256) anchor_kernel(EncArgs A, const uint8_t *__restrict__ impflags) {
   using G = Geo<F>;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= A.rows * A.nb) return;
-  const int64_t r = i / A.nb;
-  const int b = static_cast<int>(i % A.nb);
+  __shared__ float s_blk[F == IQ1_M ? 8 : 1][F == IQ1_M ? 256 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, sl = lane & 31;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 2 + half;
+  const bool live = i < A.rows * A.nb;
+  const int64_t ii = live ? i : 0;
+  const int64_t r = ii / A.nb;
+  const int b = static_cast<int>(ii % A.nb);
   const int64_t e = r / A.rpe;
-  const int64_t base = r * A.cols + static_cast<int64_t>(b) * 256;
-  int st = 0;
+  float v[8];
+  load8(A.w, A.dtype, r * A.cols + static_cast<int64_t>(b) * 256 + sl * 8, v);
   float amax = 0.0f;
-  bool finite = true;
-  for (int j8 = 0; j8 < 32; ++j8) {
-    float v[8];
-    load8(A.w, A.dtype, base + 8 * j8, v);
+  int finite = 1;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      finite = finite && finite_f(v[j]);
-      amax = fmaxf(amax, fabsf(v[j]));
-    }
+  for (int j = 0; j < 8; ++j) {
+    finite &= finite_f(v[j]) ? 1 : 0;
+    amax = fmaxf(amax, fabsf(v[j]));
   }
+  int chok = 1;
+  if (A.choices && sl < G::UNITS) chok = A.choices[ii * G::UNITS + sl] < G::NC;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o));
+    finite &= __shfl_xor(finite, o);
+    chok &= __shfl_xor(chok, o);
+  }
+  float ss = 0.0f;
+  if (F == IQ1_M) {
+    const int q = wave * 2 + half;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_blk[q][sl * 8 + j] = v[j];
+    __syncthreads();
+    if (sl == 0 && finite)
+      for (int j = 0; j < 256; ++j) ss = __builtin_fmaf(s_blk[q][j], s_blk[q][j], ss);
+  }
+  if (!live || sl != 0) return;
+  int st = 0;
   uint16_t h = 0;
   if (!finite) {
     st |= ST_NONFINITE;
@@ -89,13 +129,6 @@ __global__ void __launch_bounds__(256) anchor_kernel(EncArgs A) {
     float ratio = 1.0f;                 // IQ2: no ratio is printed on the pages; 1
     if (F == IQ1_S) ratio = 0.61f;
     if (F == IQ1_M) {                   // peak-to-RMS over the 256-value block
-      float ss = 0.0f;
-      for (int j8 = 0; j8 < 32; ++j8) {
-        float v[8];
-        load8(A.w, A.dtype, base + 8 * j8, v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
-      }
       const float rms = sqrtf(ss * (1.0f / 256.0f));
       const float p = amax / rms;
       ratio = fminf(fmaxf(__builtin_fmaf(0.035f, p, 0.58f), 0.65f), 0.95f);
@@ -110,24 +143,10 @@ __global__ void __launch_bounds__(256) anchor_kernel(EncArgs A) {
       h = 0;
     }
   }
-  if (A.imp) {
-    const float *ap = A.imp + e * A.cols + static_cast<int64_t>(b) * 256;
-    bool ok = true;
-    for (int j = 0; j < 256; j += 4) {
-      const float4 q = *reinterpret_cast<const float4 *>(ap + j);
-      ok = ok && finite_f(q.x) && finite_f(q.y) && finite_f(q.z) && finite_f(q.w) &&
-           q.x >= 0.0f && q.y >= 0.0f && q.z >= 0.0f && q.w >= 0.0f;
-    }
-    if (!ok) { st |= ST_BADIMP; h = 0; }
-  }
-  if (A.choices) {
-    const uint8_t *cp = A.choices + i * G::UNITS;
-    bool ok = true;
-    for (int u = 0; u < G::UNITS; ++u) ok = ok && cp[u] < G::NC;
-    if (!ok) { st |= ST_BADCHOICE; h = 0; }
-  }
-  A.dscr[i] = h;
-  if (F != IQ1_M) *reinterpret_cast<uint16_t *>(A.out + i * G::BYTES) = h;
+  if (impflags && impflags[e * A.nb + b]) { st |= ST_BADIMP; h = 0; }
+  if (!chok) { st |= ST_BADCHOICE; h = 0; }
+  A.dscr[ii] = h;
+  if (F != IQ1_M) *reinterpret_cast<uint16_t *>(A.out + ii * G::BYTES) = h;
   raise_status(A.status, st);
 }
 
@@ -230,6 +249,16 @@ struct GroupState {
   }
 };
 
+// Copy a wave-uniform (SGPR) value into a VGPR.  On gfx950 a VALU op that
+// reads an SGPR cannot be co-issued with another wave's VALU op, while all-VGPR
+// fp32 FMA/MUL/ADD ops can; the 16 candidate FMAs per grid entry read the
+// weighted norm, so one copy per entry lets them all co-issue.
+__device__ __forceinline__ float to_vgpr(float s) {
+  float v;
+  asm("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+  return v;
+}
+
 __device__ __forceinline__ void load_entry(const float *p, float g[8]) {
   const float4 a = *reinterpret_cast<const float4 *>(p);
   const float4 b = *reinterpret_cast<const float4 *>(p + 4);
@@ -244,7 +273,7 @@ template <int F, bool FIXED>
 __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   using G = Geo<F>;
   constexpr int WGG = G::WGG, GPU = G::GPU, N = G::N;
-  constexpr int CH = 16, NCH = N / CH;
+  constexpr int CH = 32, NCH = N / CH;
   constexpr int UPW = WGG / GPU;                 // choice units per workgroup
   constexpr int SBS = 32 / WGG;                  // workgroups per block column
   // slots swept per lane: IQ2 16 choices; IQ1 8 scales x 2 shifts;
@@ -336,7 +365,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
         for (int j = 0; j < 8; ++j) g[j] = gp[j];
         const float q2 = S.term(g);
         if (!G::IQ1) {
-          const float Gk = gt[k + p];
+          const float Gk = to_vgpr(gt[k + p]);
           if (FIXED) {
             t[0] = __builtin_fmaf(fs, Gk, q2);
           } else {
@@ -344,7 +373,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
             for (int c = 0; c < 16; ++c) t[c] = __builtin_fmaf(sc[c], Gk, q2);
           }
         } else {
-          const float G0 = gt[k + p], G1 = gt[N + k + p];
+          const float G0 = to_vgpr(gt[k + p]), G1 = to_vgpr(gt[N + k + p]);
           const float p0 = __builtin_fmaf(0.125f, S.S2, q2);
           const float p1 = __builtin_fmaf(-0.125f, S.S2, q2);
           if (FIXED) {
@@ -630,17 +659,27 @@ static int launch_quantize_t(EncArgs A, hipStream_t stream) {
   const int NG = G::IQ1 ? 2 : 1;
   const size_t gbytes = static_cast<size_t>(ntab) * NG * G::N * sizeof(float);
   const size_t dbytes = static_cast<size_t>(nblocks) * sizeof(uint16_t);
+  const size_t fbytes = A.imp ? static_cast<size_t>(A.E) * A.nb : 0;
+  const size_t goff = 0, doff = (gbytes + 255) & ~size_t(255), foff = doff + ((dbytes + 255) & ~size_t(255));
   void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, gbytes + dbytes + 256, stream) != hipSuccess) return -1;
-  A.gtab = static_cast<float *>(scratch);
-  A.dscr = reinterpret_cast<uint16_t *>(static_cast<char *>(scratch) + ((gbytes + 255) & ~size_t(255)));
+  if (hipMallocAsync(&scratch, foff + fbytes + 256, stream) != hipSuccess) return -1;
+  char *base = static_cast<char *>(scratch);
+  A.gtab = reinterpret_cast<float *>(base + goff);
+  A.dscr = reinterpret_cast<uint16_t *>(base + doff);
+  uint8_t *impflags = A.imp ? reinterpret_cast<uint8_t *>(base + foff) : nullptr;
   A.gtab_e_stride = A.imp ? cgs * NG * G::N : 0;
   A.gtab_cg_stride = A.imp ? NG * G::N : 0;
 
   const int64_t gthreads = ntab * G::N;
   hipLaunchKernelGGL(gterm_kernel<F>, dim3(static_cast<unsigned>((gthreads + 255) / 256)), dim3(256), 0, stream,
                      A.grid, A.imp, A.cols, ntab, A.gtab);
-  hipLaunchKernelGGL(anchor_kernel<F>, dim3(static_cast<unsigned>((nblocks + 255) / 256)), dim3(256), 0, stream, A);
+  if (impflags) {
+    const int64_t nf = A.E * A.nb;
+    hipLaunchKernelGGL(impcheck_kernel, dim3(static_cast<unsigned>((nf + 3) / 4)), dim3(256), 0, stream, A.imp, nf,
+                       impflags);
+  }
+  hipLaunchKernelGGL(anchor_kernel<F>, dim3(static_cast<unsigned>((nblocks + 7) / 8)), dim3(256), 0, stream, A,
+                     static_cast<const uint8_t *>(impflags));
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb * (32 / G::WGG);
   hipEvent_t ev0, ev1;
