@@ -183,6 +183,26 @@ def main() -> int:
         extras["per_format_5632x2048"] = per
         del ch
 
+        # every-choice encode: one payload per choice from a single sweep
+        ev = {}
+        for f in api.FORMATS:
+            g = torch.from_numpy(inputs.grid_for(f, GRID_SEED[f])).to(dev)
+            out = api.quantize_every_choice(f, w, g, imp)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.reps):
+                api.quantize_every_choice(f, w, g, imp, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.reps
+            nc = api.format_info(f)["num_choices"]
+            ev[f] = {"every_choice_ms": round(ms, 4), "choices": nc,
+                     "vs_one_encode": round(ms / per[f]["encode_ms"], 2)}
+            del out
+        extras["every_choice_5632x2048"] = ev
+        log("every choice", ev)
+
         # IQ1 layouts on 17408x5120 (importance from 4,096 tokens)
         wl, xl, gl, sl = inputs.workload("iq1_s_17408x5120")
         wld, xld = to_dev_bf16(wl), to_dev_bf16(xl)

@@ -30,6 +30,7 @@ SIGNATURES = {
     "iq_imatrix_collect": ([_P, _I, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "iq_imatrix_importance": ([_P, _P, _I, _I64, _F, _P, _P, _P], _I),
     "iq_quantize": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
+    "iq_quantize_every_choice": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "iq_dequantize": ([_I, _P, _I64, _I64, _P, _P, _I, _P], _I),
     "iq_time_next_search": ([_P, _P], _I),
     "iq_error_string": ([_I], ctypes.c_char_p),
@@ -183,6 +184,36 @@ def quantize(fmt, w: torch.Tensor, grid: torch.Tensor, importance: torch.Tensor 
         st = read_status(status)
         if st:
             raise IQError(f"iq_quantize device status {st:#x}")
+    return out
+
+
+def quantize_every_choice(fmt, w: torch.Tensor, grid: torch.Tensor, importance: torch.Tensor | None = None,
+                          rows_per_expert: int | None = None, out: torch.Tensor | None = None,
+                          status: torch.Tensor | None = None) -> torch.Tensor:
+    """Encode w under every choice: uint8 [num_choices, rows, cols/256, block_bytes],
+    out[c] == quantize(fmt, w, grid, importance, choices=full(c))."""
+    f = _fmt(fmt)
+    if w.dim() != 2:
+        raise IQError("w must be [rows, cols]")
+    rows, cols = w.shape
+    info = format_info(f)
+    if tuple(grid.shape) != (info["grid_size"], 8):
+        raise IQError(f"grid must be [{info['grid_size']}, 8]")
+    rpe = rows if rows_per_expert is None else int(rows_per_expert)
+    if importance is not None and (rpe < 1 or importance.dim() != 2 or importance.shape[1] != cols
+                                   or importance.shape[0] * rpe != rows):
+        raise IQError("importance must be [rows / rows_per_expert, cols]")
+    if out is None:
+        out = torch.empty((info["num_choices"], rows, cols // 256, info["block_bytes"]), dtype=torch.uint8,
+                          device=w.device)
+    if w.dtype not in DTYPE:
+        raise IQError(f"unsupported dtype {w.dtype}")
+    rc = lib().iq_quantize_every_choice(f, _dev(w, "w"), DTYPE[w.dtype], rows, cols, rpe,
+                                        _dev(grid, "grid", torch.float32),
+                                        _dev(importance, "importance", torch.float32),
+                                        _dev(out, "out", torch.uint8), _dev(status, "status", torch.int32),
+                                        _stream())
+    _check(rc, "iq_quantize_every_choice")
     return out
 
 

@@ -73,9 +73,9 @@ int iq_imatrix_importance(const float *sums, const int64_t *counts, int num_expe
              : IQ_ERR_HIP;
 }
 
-int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
-                const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
-                int32_t *status, hipStream_t stream) {
+static int quantize_common(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                           const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
+                           int32_t *status, bool every, hipStream_t stream) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
   if (!w || !grid || !out) return IQ_ERR_NULL;
@@ -94,12 +94,28 @@ int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, i
   A.imp = importance;
   A.choices = choices;
   A.out = out;
+  A.copies = every ? kFmt[fmt].num_choices : 1;
+  A.copy_stride = rows * (cols / 256) * kFmt[fmt].block_bytes;
   A.status = status;
   // workgroups: experts x 64-row tiles x column sets; must fit one grid dimension
   const int64_t wgg = (fmt == IQ_FMT_IQ1_M) ? 8 : 4;
   const int64_t total = A.E * ((rows_per_expert + 63) / 64) * A.nb * (32 / wgg);
   if (total >= (int64_t(1) << 31)) return IQ_ERR_SHAPE;
-  return iq::launch_quantize(fmt, A, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
+  return iq::launch_quantize(fmt, A, every, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
+}
+
+int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
+                int32_t *status, hipStream_t stream) {
+  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, choices, out, status, false,
+                         stream);
+}
+
+int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                             const float *grid, const float *importance, uint8_t *out, int32_t *status,
+                             hipStream_t stream) {
+  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, nullptr, out, status, true,
+                         stream);
 }
 
 int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,

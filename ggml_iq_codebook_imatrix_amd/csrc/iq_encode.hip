@@ -146,7 +146,8 @@ __global__ void __launch_bounds__(256) anchor_kernel(EncArgs A, const uint8_t *_
   if (impflags && impflags[e * A.nb + b]) { st |= ST_BADIMP; h = 0; }
   if (!chok) { st |= ST_BADCHOICE; h = 0; }
   A.dscr[ii] = h;
-  if (F != IQ1_M) *reinterpret_cast<uint16_t *>(A.out + ii * G::BYTES) = h;
+  if (F != IQ1_M)
+    for (int64_t c = 0; c < A.copies; ++c) *reinterpret_cast<uint16_t *>(A.out + c * A.copy_stride + ii * G::BYTES) = h;
   raise_status(A.status, st);
 }
 
@@ -267,11 +268,117 @@ __device__ __forceinline__ void load_entry(const float *p, float g[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// Rescan one 32-entry chunk under one (scale, shift) slot: the first entry with
+// the least reduced error -- the same fp32 values the sweep compared -- and
+// its sign mask (IQ2) or shift bit (IQ1).
+// ---------------------------------------------------------------------------
+template <int F>
+__device__ __forceinline__ void rescan_chunk(const float *__restrict__ grid, const float *gt, const GroupState<F> &S,
+                                             int chs, float ssel, int hsel, int &kb, uint32_t &mfield) {
+  using G = Geo<F>;
+  constexpr int CH = 32, N = G::N;
+  const float dsel = hsel ? -0.125f : 0.125f;
+  float bt = __builtin_inff();
+  kb = chs * CH;
+  for (int i = 0; i < CH; ++i) {
+    const int k = chs * CH + i;
+    float g[8];
+    load_entry(grid + static_cast<int64_t>(k) * 8, g);
+    const float q2 = S.term(g);
+    float t;
+    if (!G::IQ1) {
+      t = __builtin_fmaf(ssel, gt[k], q2);
+    } else {
+      const float pn = __builtin_fmaf(dsel, S.S2, q2);
+      t = __builtin_fmaf(ssel, gt[hsel * N + k], pn);
+    }
+    if (t < bt) { bt = t; kb = k; }
+  }
+  if (!G::IQ1) {
+    uint32_t mask = S.neg;
+    if (S.odd) {
+      float g[8];
+      load_entry(grid + static_cast<int64_t>(kb) * 8, g);
+      mask ^= 1u << S.flip_index(g);
+    }
+    mfield = mask;
+  } else {
+    mfield = static_cast<uint32_t>(hsel);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pack one workgroup's bytes of one row's block from the LDS field tables:
+// k[g][row], m[g][row] (IQ2 sign mask / IQ1 shift), c[u][row] (unit choice).
+// Workgroup sb owns: IQ2_XXS/XS/S, IQ1_S the 32-value sub-block sb; IQ1_M the
+// 64 values of scale word sb.
+// ---------------------------------------------------------------------------
+template <int F>
+__device__ __forceinline__ void pack_bytes(uint8_t *blk, int sb, int lane, const uint16_t (*s_k)[64],
+                                           const uint8_t (*s_m)[64], const uint8_t (*s_c)[64], uint32_t d16) {
+  if (F == IQ2_XXS) {  // 4 index bytes, then (4 x 7-bit sign index | scale << 28)
+    uint8_t *p = blk + 2 + 8 * sb;
+    uint32_t word = static_cast<uint32_t>(s_c[0][lane]) << 28;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      p[l] = static_cast<uint8_t>(s_k[l][lane]);
+      word |= (static_cast<uint32_t>(s_m[l][lane]) & 0x7fu) << (7 * l);
+    }
+    reinterpret_cast<uint16_t *>(p + 4)[0] = static_cast<uint16_t>(word);
+    reinterpret_cast<uint16_t *>(p + 4)[1] = static_cast<uint16_t>(word >> 16);
+  } else if (F == IQ2_XS) {  // 4 x (9-bit index | 7-bit sign index << 9), scale byte
+#pragma unroll
+    for (int l = 0; l < 4; ++l)
+      reinterpret_cast<uint16_t *>(blk + 2 + 2 * (4 * sb + l))[0] =
+          static_cast<uint16_t>(s_k[l][lane] | ((s_m[l][lane] & 0x7fu) << 9));
+    blk[66 + sb] = static_cast<uint8_t>(s_c[0][lane] | (s_c[1][lane] << 4));
+  } else if (F == IQ2_S) {  // low index bytes, sign masks, high index bits, scale byte
+    uint32_t hi = 0;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      blk[2 + 4 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
+      blk[34 + 4 * sb + l] = s_m[l][lane];
+      hi |= ((s_k[l][lane] >> 8) & 3u) << (2 * l);
+    }
+    blk[66 + sb] = static_cast<uint8_t>(hi);
+    blk[74 + sb] = static_cast<uint8_t>(s_c[0][lane] | (s_c[1][lane] << 4));
+  } else if (F == IQ1_S) {  // low index bytes, (4 x 3 high bits | scale << 12 | shift << 15)
+    const uint32_t c = s_c[0][lane];
+    uint32_t w = ((c & 7u) << 12) | ((c >> 3) << 15);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      blk[2 + 4 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
+      w |= ((s_k[l][lane] >> 8) & 7u) << (3 * l);
+    }
+    reinterpret_cast<uint16_t *>(blk + 34 + 2 * sb)[0] = static_cast<uint16_t>(w);
+  } else {  // IQ1_M, 8 groups: low index bytes, qh nibbles, scale word with d nibble sb
+#pragma unroll
+    for (int l = 0; l < 8; ++l) blk[8 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint32_t lo = ((s_k[2 * qq][lane] >> 8) & 7u) | (static_cast<uint32_t>(s_m[2 * qq][lane]) << 3);
+      const uint32_t hi = ((s_k[2 * qq + 1][lane] >> 8) & 7u) | (static_cast<uint32_t>(s_m[2 * qq + 1][lane]) << 3);
+      blk[32 + 4 * sb + qq] = static_cast<uint8_t>(lo | (hi << 4));
+    }
+    uint32_t w = ((d16 >> (4 * sb)) & 0xfu) << 12;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w |= (s_c[u][lane] & 7u) << (3 * u);
+    reinterpret_cast<uint16_t *>(blk + 48 + 2 * sb)[0] = static_cast<uint16_t>(w);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Search + pack.  Workgroup = WGG waves (groups) x 64 rows of one expert.
 // ---------------------------------------------------------------------------
-template <int F, bool FIXED>
+// MODE: SEARCH scores every choice per unit; FIXED takes the caller's choices;
+// EVERY writes one payload per choice (out[c] == the FIXED payload with every
+// unit set to c) from a single sweep.
+enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2 };
+
+template <int F, int MODE>
 __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   using G = Geo<F>;
+  constexpr bool FIXED = MODE == FIXED_CHOICES;
   constexpr int WGG = G::WGG, GPU = G::GPU, N = G::N;
   constexpr int CH = 32, NCH = N / CH;
   constexpr int UPW = WGG / GPU;                 // choice units per workgroup
@@ -280,7 +387,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   // fixed choices: one slot (IQ1_M: its two shifts)
   constexpr int NSLOT = FIXED ? (F == IQ1_M ? 2 : 1) : 16;
 
-  __shared__ float s_best[FIXED ? 1 : WGG][FIXED ? 1 : NSLOT][64];
+  __shared__ float s_best[MODE == SEARCH ? WGG : 1][MODE == SEARCH ? NSLOT : 1][64];
   __shared__ uint16_t s_k[WGG][64];
   __shared__ uint8_t s_m[WGG][64];
   __shared__ uint8_t s_c[UPW][64];
@@ -404,6 +511,31 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
     }
   }
 
+  // ---- every choice: one payload per choice --------------------------------
+  if (MODE == EVERY) {
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+      int slot = c;
+      if (F == IQ1_M) slot = (best[8 + c] < best[c]) ? 8 + c : c;  // tie: the lower shift
+      int chs = bidx[c];
+      if (F == IQ1_M) chs = (slot != c) ? bidx[8 + c] : chs;
+      const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
+      int kb;
+      uint32_t mfield;
+      rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      int cu = c;
+      if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
+      __syncthreads();  // the previous choice's bytes have been read from LDS
+      s_k[wave][lane] = static_cast<uint16_t>(kb);
+      s_m[wave][lane] = static_cast<uint8_t>(mfield);
+      if (wave % GPU == 0) s_c[uw][lane] = static_cast<uint8_t>(cu);
+      __syncthreads();
+      if (wave == 0 && valid)
+        pack_bytes<F>(A.out + c * A.copy_stride + (r * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, d16);
+    }
+    return;
+  }
+
   // ---- choice per unit ---------------------------------------------------
   int cu = 0;     // unit choice (IQ1_S: (h << 3) | ls)
   int slot = 0;   // slot of this lane's group under that choice
@@ -453,16 +585,14 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
 
   // ---- rescan the chosen chunk for the exact entry ----------------------
   int chs = bidx[0];
+#pragma unroll
+  for (int s = 1; s < NSLOT; ++s) chs = (slot == s) ? bidx[s] : chs;
   float ssel;
   int hsel;
   if (FIXED) {
-#pragma unroll
-    for (int s = 1; s < NSLOT; ++s) chs = (slot == s) ? bidx[s] : chs;
     ssel = fs;
     hsel = (F == IQ1_M) ? slot : fh;
   } else {
-#pragma unroll
-    for (int s = 1; s < NSLOT; ++s) chs = (slot == s) ? bidx[s] : chs;
     ssel = sc[0];
     if (!G::IQ1) {
 #pragma unroll
@@ -473,35 +603,9 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
     }
     hsel = G::IQ1 ? (slot >> 3) : 0;
   }
-  const float dsel = hsel ? -0.125f : 0.125f;
-  float bt = __builtin_inff();
-  int kb = chs * CH;
-  for (int i = 0; i < CH; ++i) {
-    const int k = chs * CH + i;
-    float g[8];
-    load_entry(A.grid + static_cast<int64_t>(k) * 8, g);
-    const float q2 = S.term(g);
-    float t;
-    if (!G::IQ1) {
-      t = __builtin_fmaf(ssel, gt[k], q2);
-    } else {
-      const float pn = __builtin_fmaf(dsel, S.S2, q2);
-      t = __builtin_fmaf(ssel, gt[hsel * N + k], pn);
-    }
-    if (t < bt) { bt = t; kb = k; }
-  }
+  int kb;
   uint32_t mfield;
-  if (!G::IQ1) {
-    uint32_t mask = S.neg;
-    if (S.odd) {
-      float g[8];
-      load_entry(A.grid + static_cast<int64_t>(kb) * 8, g);
-      mask ^= 1u << S.flip_index(g);
-    }
-    mfield = mask;
-  } else {
-    mfield = static_cast<uint32_t>(hsel);
-  }
+  rescan_chunk<F>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
   if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
 
   // ---- pack ----------------------------------------------------------------
@@ -510,56 +614,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   if (wave % GPU == 0) s_c[uw][lane] = static_cast<uint8_t>(cu);
   __syncthreads();
   if (wave != 0 || !valid) return;
-  uint8_t *blk = A.out + (r * A.nb + b) * G::BYTES;
-  if (F == IQ2_XXS) {  // sub-block sb: 4 index bytes, then (4 x 7-bit sign index | scale << 28)
-    uint8_t *p = blk + 2 + 8 * sb;
-    uint32_t word = static_cast<uint32_t>(s_c[0][lane]) << 28;
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      p[l] = static_cast<uint8_t>(s_k[l][lane]);
-      word |= (static_cast<uint32_t>(s_m[l][lane]) & 0x7fu) << (7 * l);
-    }
-    reinterpret_cast<uint16_t *>(p + 4)[0] = static_cast<uint16_t>(word);
-    reinterpret_cast<uint16_t *>(p + 4)[1] = static_cast<uint16_t>(word >> 16);
-  } else if (F == IQ2_XS) {  // 4 x (9-bit index | 7-bit sign index << 9), scale byte
-#pragma unroll
-    for (int l = 0; l < 4; ++l)
-      reinterpret_cast<uint16_t *>(blk + 2 + 2 * (4 * sb + l))[0] =
-          static_cast<uint16_t>(s_k[l][lane] | ((s_m[l][lane] & 0x7fu) << 9));
-    blk[66 + sb] = static_cast<uint8_t>(s_c[0][lane] | (s_c[1][lane] << 4));
-  } else if (F == IQ2_S) {  // low index bytes, sign masks, high index bits, scale byte
-    uint32_t hi = 0;
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      blk[2 + 4 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
-      blk[34 + 4 * sb + l] = s_m[l][lane];
-      hi |= ((s_k[l][lane] >> 8) & 3u) << (2 * l);
-    }
-    blk[66 + sb] = static_cast<uint8_t>(hi);
-    blk[74 + sb] = static_cast<uint8_t>(s_c[0][lane] | (s_c[1][lane] << 4));
-  } else if (F == IQ1_S) {  // low index bytes, (4 x 3 high bits | scale << 12 | shift << 15)
-    const uint32_t c = s_c[0][lane];
-    uint32_t w = ((c & 7u) << 12) | ((c >> 3) << 15);
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      blk[2 + 4 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
-      w |= ((s_k[l][lane] >> 8) & 7u) << (3 * l);
-    }
-    reinterpret_cast<uint16_t *>(blk + 34 + 2 * sb)[0] = static_cast<uint16_t>(w);
-  } else {  // IQ1_M, 8 groups: low index bytes, qh nibbles, scale word with d nibble sb
-#pragma unroll
-    for (int l = 0; l < 8; ++l) blk[8 * sb + l] = static_cast<uint8_t>(s_k[l][lane] & 0xff);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const uint32_t lo = ((s_k[2 * qq][lane] >> 8) & 7u) | (static_cast<uint32_t>(s_m[2 * qq][lane]) << 3);
-      const uint32_t hi = ((s_k[2 * qq + 1][lane] >> 8) & 7u) | (static_cast<uint32_t>(s_m[2 * qq + 1][lane]) << 3);
-      blk[32 + 4 * sb + qq] = static_cast<uint8_t>(lo | (hi << 4));
-    }
-    uint32_t w = ((static_cast<uint32_t>(d16) >> (4 * sb)) & 0xfu) << 12;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) w |= (s_c[u][lane] & 7u) << (3 * u);
-    reinterpret_cast<uint16_t *>(blk + 48 + 2 * sb)[0] = static_cast<uint16_t>(w);
-  }
+  pack_bytes<F>(A.out + (r * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, d16);
 }
 
 // ---------------------------------------------------------------------------
@@ -650,7 +705,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
 // Host launchers
 // ---------------------------------------------------------------------------
 template <int F>
-static int launch_quantize_t(EncArgs A, hipStream_t stream) {
+static int launch_quantize_t(EncArgs A, bool every, hipStream_t stream) {
   using G = Geo<F>;
   const int64_t nblocks = A.rows * A.nb;
   if (nblocks == 0) return 0;
@@ -685,25 +740,26 @@ static int launch_quantize_t(EncArgs A, hipStream_t stream) {
   hipEvent_t ev0, ev1;
   take_search_events(&ev0, &ev1);
   if (ev0) hipEventRecord(ev0, stream);
-  if (A.choices)
-    hipLaunchKernelGGL((search_kernel<F, true>), dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::WGG), 0,
-                       stream, A);
+  const dim3 grid_dim(static_cast<unsigned>(A.total_wg)), block_dim(64 * G::WGG);
+  if (every)
+    hipLaunchKernelGGL((search_kernel<F, EVERY>), grid_dim, block_dim, 0, stream, A);
+  else if (A.choices)
+    hipLaunchKernelGGL((search_kernel<F, FIXED_CHOICES>), grid_dim, block_dim, 0, stream, A);
   else
-    hipLaunchKernelGGL((search_kernel<F, false>), dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::WGG), 0,
-                       stream, A);
+    hipLaunchKernelGGL((search_kernel<F, SEARCH>), grid_dim, block_dim, 0, stream, A);
   const hipError_t le = hipGetLastError();
   if (ev1) hipEventRecord(ev1, stream);
   hipFreeAsync(scratch, stream);
   return le == hipSuccess ? 0 : -1;
 }
 
-int launch_quantize(int fmt, EncArgs A, hipStream_t stream) {
+int launch_quantize(int fmt, EncArgs A, bool every, hipStream_t stream) {
   switch (fmt) {
-    case IQ2_XXS: return launch_quantize_t<IQ2_XXS>(A, stream);
-    case IQ2_XS: return launch_quantize_t<IQ2_XS>(A, stream);
-    case IQ2_S: return launch_quantize_t<IQ2_S>(A, stream);
-    case IQ1_S: return launch_quantize_t<IQ1_S>(A, stream);
-    case IQ1_M: return launch_quantize_t<IQ1_M>(A, stream);
+    case IQ2_XXS: return launch_quantize_t<IQ2_XXS>(A, every, stream);
+    case IQ2_XS: return launch_quantize_t<IQ2_XS>(A, every, stream);
+    case IQ2_S: return launch_quantize_t<IQ2_S>(A, every, stream);
+    case IQ1_S: return launch_quantize_t<IQ1_S>(A, every, stream);
+    case IQ1_M: return launch_quantize_t<IQ1_M>(A, every, stream);
   }
   return -1;
 }

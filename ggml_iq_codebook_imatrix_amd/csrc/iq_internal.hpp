@@ -16,6 +16,7 @@ struct EncArgs {
   const float *imp;        // [E, cols] or null (flat)
   const uint8_t *choices;  // [rows, nb, units] or null
   uint8_t *out;
+  int64_t copies, copy_stride;  // payload copies (every-choice: num_choices) and bytes between them
   int32_t *status;
   // filled by the launcher
   float *gtab;             // weighted norms [tables][NG][N]
@@ -27,7 +28,7 @@ struct EncArgs {
 // events registered by iq_time_next_search for this host thread (cleared on take)
 void take_search_events(hipEvent_t *start, hipEvent_t *stop);
 
-int launch_quantize(int fmt, EncArgs A, hipStream_t stream);
+int launch_quantize(int fmt, EncArgs A, bool every_choice, hipStream_t stream);
 int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
                   int dtype, hipStream_t stream);
 int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,

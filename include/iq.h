@@ -155,6 +155,17 @@ int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
                 int64_t rows_per_expert, const float *grid, const float *importance,
                 const uint8_t *choices, uint8_t *out, int32_t *status, hipStream_t stream);
 
+/* Every-choice encode ([3157] series, squashed #3159 "one-pass every-choice
+ * encode": each 256-column block encoded under every choice from a single
+ * sweep, byte-identical to the forced encodes).
+ *  out (device) [num_choices, rows, cols/256, block_bytes]: out[c] is exactly
+ *  the payload iq_quantize writes with `choices` set to c for every unit
+ *  (IQ1_S: c = (delta_sign << 3) | local scale).
+ *  Other arguments, status bits and errors as iq_quantize (no `choices`). */
+int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
+                             int64_t rows_per_expert, const float *grid, const float *importance,
+                             uint8_t *out, int32_t *status, hipStream_t stream);
+
 /* Decode ([2513]: dequantize_row semantics; IQ1_M d reassembled from the top
  * nibbles of the four scale words, one 3-bit scale per two groups).
  *  packed (device) [rows, cols/256, block_bytes]; grid (device) [grid_size, 8];

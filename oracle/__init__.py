@@ -177,6 +177,22 @@ def quantize(fmt, w, grid, importance=None, rows_per_expert=None, choices=None, 
     return out, st
 
 
+def quantize_every_choice(fmt, w, grid, importance=None, rows_per_expert=None, row_ids=None,
+                          threads: int | None = None):
+    """[num_choices, n_rows, cols/256, block_bytes]: for each choice c, the encode with
+    every unit fixed to c (ModelOpt PR #3159 description: the PyTorch encoders loop over
+    forced choices; packed[c] == quantize(choices=full(c)))."""
+    geo = geometry(fmt)
+    rows, cols = np.asarray(w).shape
+    outs, st = [], 0
+    for c in range(geo["num_choices"]):
+        ch = np.full((rows, cols // 256, geo["units"]), c, np.uint8)
+        p, s = quantize(fmt, w, grid, importance, rows_per_expert, choices=ch, row_ids=row_ids, threads=threads)
+        outs.append(p)
+        st |= s
+    return np.stack(outs), st
+
+
 def dequantize(fmt, packed, rows, cols, grid):
     p = np.ascontiguousarray(packed, dtype=np.uint8)
     y = np.empty((rows, cols), dtype=np.float32)

@@ -31,8 +31,8 @@ def api():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["iq_format_info", "iq_imatrix_collect", "iq_imatrix_importance", "iq_quantize", "iq_dequantize",
-         "iq_time_next_search", "iq_error_string"])
+        ["iq_format_info", "iq_imatrix_collect", "iq_imatrix_importance", "iq_quantize",
+         "iq_quantize_every_choice", "iq_dequantize", "iq_time_next_search", "iq_error_string"])
 
 
 def test_library_exports_every_declared_symbol(api):
@@ -66,6 +66,9 @@ def test_host_validation_quantize(api):
     assert q(w=None) == -3 and q(grid=None) == -3 and q(out=None) == -3
     assert q(cols=300) == -4 and q(cols=0) == -4 and q(rows=-1) == -4
     assert q(rpe=0) == -4 and q(rpe=48) == -4
+    ev = lambda fmt=0, cols=512, out=FAKE: L.iq_quantize_every_choice(fmt, FAKE, 1, 64, cols, 64, FAKE, None, out,
+                                                                      None, None)
+    assert ev(fmt=7) == -1 and ev(cols=100) == -4 and ev(out=None) == -3
     assert L.iq_format_info(0, None) == -3
     assert api.lib().iq_error_string(-4) == b"invalid shape"
     assert L.iq_time_next_search(FAKE, None) == -3 and L.iq_time_next_search(None, FAKE) == -3

@@ -132,6 +132,43 @@ def test_encode_edge_blocks(api, orc, fmt):
     assert st == st_o == 4 and np.array_equal(got, want) and not got[4, 1].any()
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_every_choice_parity(api, orc, fmt):
+    """out[c] == the encode with every unit fixed to c (ModelOpt PR #3159), both
+    against the GPU's own fixed-choice path and the oracle; experts with ragged
+    tiles, one of them idle (flat weights), plus an all-zero block."""
+    say("every choice", fmt)
+    geo = orc.geometry(fmt)
+    grid = inputs.grid_for(fmt, GRID_SEED[fmt])
+    rows, cols, rpe = 2 * 68, 512, 68
+    w = inputs.weight(rows, cols, 2100, 2101)
+    w[5, :256] = 0.0
+    imp = np.stack([inputs.importance_like(cols, 2102), np.ones(cols, np.float32)])
+    wd, gd, idd = dev_w(w, "bf16"), dev(grid), dev(imp)
+    st = api.new_status()
+    every = host(api.quantize_every_choice(fmt, wd, gd, idd, rows_per_expert=rpe, status=st))
+    assert int(host(st)[0]) == 0
+    assert every.shape == (geo["num_choices"], rows, cols // 256, geo["block_bytes"])
+    want, _ = orc.quantize_every_choice(fmt, w, grid, imp, rows_per_expert=rpe)
+    for c in range(geo["num_choices"]):
+        fixed = host(api.quantize(fmt, wd, gd, idd, rows_per_expert=rpe,
+                                  choices=dev(np.full((rows, cols // 256, geo["units"]), c, np.uint8))))
+        assert np.array_equal(every[c], fixed), c
+        assert np.array_equal(every[c], want[c]), c
+    assert not every[:, 5, 0].any()
+
+
+def test_every_choice_full_size_sampled(api, orc):
+    say("every choice full size IQ2_XS")
+    w, x, grid, spec = inputs.workload("iq2_xs_5632x2048")
+    sums, counts = api.imatrix_collect(dev_w(x, "bf16"), chunk_rows=1024)
+    imp = api.imatrix_importance(sums, counts)
+    every = host(api.quantize_every_choice("IQ2_XS", dev_w(w, "bf16"), dev(grid), imp))
+    rid = np.sort(inputs.rng(2200).choice(w.shape[0], 12, replace=False))
+    want, _ = orc.quantize_every_choice("IQ2_XS", w, grid, host(imp), row_ids=rid)
+    assert np.array_equal(every[:, rid], want)
+
+
 def test_encode_is_deterministic(api):
     say("determinism")
     fmt = "IQ2_S"
