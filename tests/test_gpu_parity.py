@@ -305,9 +305,10 @@ def test_workload_iq2_xxs_256x512_end_to_end(api, orc):
 
 @pytest.mark.parametrize("name", ["iq2_xs_5632x2048", "iq2_s_5632x2048", "iq2_xxs_5632x2048",
                                   "iq1_s_5632x2048", "iq1_m_5632x2048"])
-def test_workload_full_size_sampled_rows(api, orc, name):
-    """Full 5632x2048 encode in the benchmark's launch configuration; sampled rows
-    against the oracle, plus the fixed-choice variant (every unit choice 7)."""
+def test_workload_full_size(api, orc, name):
+    """Full 5632x2048 encode in the benchmark's launch configuration against the
+    oracle (every row for the IQ2 layouts, 96 sampled rows for IQ1), plus the
+    fixed-choice variant (every unit choice 7)."""
     say("workload", name)
     w, x, grid, spec = inputs.workload(name)
     fmt = spec["fmt"]
@@ -316,17 +317,33 @@ def test_workload_full_size_sampled_rows(api, orc, name):
     imp_h = host(imp)
     wd = dev_w(w, "bf16")
     got = host(api.quantize(fmt, wd, dev(grid), imp))
-    n = 24 if fmt.startswith("IQ1") else 48
-    rid = np.sort(inputs.rng(1800).choice(w.shape[0], n, replace=False))
-    rid[-1] = w.shape[0] - 1
-    want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid)
-    assert np.array_equal(got[rid], want)
+    if fmt.startswith("IQ1"):  # sampled rows (the oracle's IQ1 search is ~10x the IQ2 cost)
+        rid = np.sort(inputs.rng(1800).choice(w.shape[0], 96, replace=False))
+        rid[-1] = w.shape[0] - 1
+    else:                      # every row
+        rid = np.arange(w.shape[0])
+    want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid, threads=16)
+    bad = np.argwhere((got[rid] != want).any(axis=2))
+    assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
     if fmt == "IQ2_S":
         geo = orc.geometry(fmt)
         ch = np.full((w.shape[0], w.shape[1] // 256, geo["units"]), 7, np.uint8)
         got7 = host(api.quantize(fmt, wd, dev(grid), imp, choices=dev(ch)))
         want7, _ = orc.quantize(fmt, w, grid, imp_h, choices=ch, row_ids=rid)
         assert np.array_equal(got7[rid], want7)
+
+
+@pytest.mark.parametrize("fmt", ["IQ1_S", "IQ1_M"])
+def test_workload_iq1_17408x5120_sampled_rows(api, orc, fmt):
+    """The larger IQ1 workload: 17408x5120 bf16, importance from 4,096 tokens."""
+    say("workload 17408x5120", fmt)
+    w, x, grid, spec = inputs.workload("iq1_s_17408x5120")
+    sums, counts = api.imatrix_collect(dev_w(x, "bf16"), chunk_rows=1024)
+    imp = api.imatrix_importance(sums, counts)
+    got = host(api.quantize(fmt, dev_w(w, "bf16"), dev(grid), imp))
+    rid = np.sort(inputs.rng(1850).choice(w.shape[0], 16, replace=False))
+    want, _ = orc.quantize(fmt, w, grid, host(imp), row_ids=rid, threads=16)
+    assert np.array_equal(got[rid], want)
 
 
 def test_workload_moe_experts(api, orc):
