@@ -60,6 +60,9 @@ def lib():
         L.orc_group_minima.argtypes = [ci, P, P, P, ci, ctypes.c_uint16, P, P]
         L.orc_quantize.argtypes = [ci, P, i64, i64, i64, P, i64, P, P, P, P, ci]
         L.orc_dequantize.argtypes = [ci, P, i64, i64, P, P]
+        L.orc_choice_search.argtypes = [ci, P, i64, i64, i64, P, i64, P, P, P, ctypes.c_float, P, ci]
+        L.orc_damping.argtypes = [P, ctypes.c_float]
+        L.orc_damping.restype = ctypes.c_float
         L.orc_pack_flat.argtypes = [ci, P, P]
         L.orc_unpack_flat.argtypes = [ci, P, P]
         _lib = L
@@ -191,6 +194,34 @@ def quantize_every_choice(fmt, w, grid, importance=None, rows_per_expert=None, r
         outs.append(p)
         st |= s
     return np.stack(outs), st
+
+
+def choice_search(fmt, w, grid, hess, importance=None, rows_per_expert=None, perc_damp: float = 0.3,
+                  row_ids=None, threads: int | None = None):
+    """Local-Hessian choice search (ModelOpt PR #3158). hess: [E, cols/256, 256, 256]
+    diagonal blocks of each expert's input Hessian.  Returns uint8 choices
+    [n_rows, cols/256, units] to feed quantize(choices=...)."""
+    f = fmt_id(fmt)
+    geo = geometry(f)
+    w = _f32(w)
+    rows, cols = w.shape
+    rpe = rows if rows_per_expert is None else int(rows_per_expert)
+    imp = None if importance is None else _f32(importance)
+    h = _f32(hess)
+    assert h.shape == (rows // rpe, cols // 256, 256, 256)
+    rid = None if row_ids is None else np.ascontiguousarray(row_ids, dtype=np.int64)
+    n = rows if rid is None else rid.size
+    out = np.zeros((n, cols // 256, geo["units"]), dtype=np.uint8)
+    threads = threads or os.cpu_count() or 1
+    st = lib().orc_choice_search(f, _p(w), rows, cols, rpe, _p(rid), n, _p(_f32(grid)), _p(imp), _p(h),
+                                 float(perc_damp), _p(out), int(threads))
+    if st < 0:
+        raise ValueError("oracle rejected the shapes")
+    return out, st
+
+
+def damping(H, perc_damp: float = 0.3) -> float:
+    return float(lib().orc_damping(_p(_f32(H)), float(perc_damp)))
 
 
 def dequantize(fmt, packed, rows, cols, grid):

@@ -736,3 +736,157 @@ int orc_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, c
       orc_decode_block(fmt, packed + (r * nb + b) * GEOM[fmt].block_bytes, grid, y + r * cols + b * 256);
   return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Local-Hessian choice search  ([3158] "local_hessian for GGML IQ": encode    */
+/* each block under every choice; give each choice unit its best choice under */
+/* its own diagonal Hessian block; revisit the units twice, each taking the   */
+/* choice that most lowers the block's error dw H dw^T with the others held;  */
+/* Hessian blocks damped by perc_damp, as GPTQ damps).                        */
+/*                                                                           */
+/* Readings: R16 the damped block is H + lambda I with lambda =              */
+/* perc_damp * (sum_j H_jj / 256) (the sum in fp64, ascending j, the mean     */
+/* rounded to fp32); R17 dw = w - w^ with w^ the decoder's values; the unit   */
+/* error is e = sum_i dw_i (sum_j H_ij dw_j), inner and outer sums fmaf       */
+/* chains in ascending index; R18 in the two passes unit u takes the first    */
+/* choice minimising f = fmaf(2, dw_u . r_u, e_u) where r_u,i = sum over the  */
+/* block's columns j outside u (ascending) of H_ij dw_j at the current picks; */
+/* a pick takes effect at once (units visited in ascending order).            */
+/* ------------------------------------------------------------------------- */
+static float hd(const float *H, float lam, int i, int j) {
+  float v = H[i * 256 + j];
+  return i == j ? v + lam : v;
+}
+
+float orc_damping(const float *H, float perc_damp) {
+  double acc = 0.0;
+  for (int j = 0; j < 256; ++j) acc += (double)H[j * 256 + j];
+  float mean = (float)(acc / 256.0);
+  return perc_damp * mean;
+}
+
+/* unit error e = dw_u Hd_uu dw_u^T over columns [c0, c0 + n) */
+static float unit_error(const float *H, float lam, const float *dw, int c0, int n) {
+  float e = 0.0f;
+  for (int i = c0; i < c0 + n; ++i) {
+    float y = 0.0f;
+    for (int j = c0; j < c0 + n; ++j) y = fmaf(hd(H, lam, i, j), dw[j], y);
+    e = fmaf(dw[i], y, e);
+  }
+  return e;
+}
+
+/* choices for one block.  x: 256 weights; a: 256 importance; H: 256x256. */
+static int choice_search_block(int fmt, const float *x, const float *a, const float *grid, const float *H,
+                               float perc_damp, uint8_t *choices, orc_scratch *sc) {
+  const orc_geom *G = &GEOM[fmt];
+  const int NC = G->nchoices, U = G->units, UV = 8 * G->gpu;
+  float *dwc = (float *)malloc(sizeof(float) * 256 * (size_t)NC);  /* dw under each choice */
+  uint8_t blk[128], ch[16];
+  float yhat[256];
+  int st = 0;
+  for (int c = 0; c < NC; ++c) {
+    for (int u = 0; u < U; ++u) ch[u] = (uint8_t)c;
+    st |= encode_block(fmt, x, a, grid, G->grid_n, ch, -1, blk, sc);
+    orc_decode_block(fmt, blk, grid, yhat);
+    for (int j = 0; j < 256; ++j) dwc[c * 256 + j] = x[j] - yhat[j];
+  }
+  const float lam = orc_damping(H, perc_damp);
+  int pick[16];
+  float dwcur[256];
+  for (int u = 0; u < U; ++u) { /* own block */
+    float best = 0.0f;
+    pick[u] = 0;
+    for (int c = 0; c < NC; ++c) {
+      float e = unit_error(H, lam, dwc + c * 256, u * UV, UV);
+      if (c == 0 || e < best) { best = e; pick[u] = c; }
+    }
+    for (int j = u * UV; j < (u + 1) * UV; ++j) dwcur[j] = dwc[pick[u] * 256 + j];
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int u = 0; u < U; ++u) {
+      float r[32];
+      for (int i = 0; i < UV; ++i) {
+        float acc = 0.0f;
+        for (int j = 0; j < 256; ++j) {
+          if (j >= u * UV && j < (u + 1) * UV) continue;
+          acc = fmaf(hd(H, lam, u * UV + i, j), dwcur[j], acc);
+        }
+        r[i] = acc;
+      }
+      float best = 0.0f;
+      int bc = 0;
+      for (int c = 0; c < NC; ++c) {
+        const float *dw = dwc + c * 256;
+        float e = unit_error(H, lam, dw, u * UV, UV);
+        float dot = 0.0f;
+        for (int i = 0; i < UV; ++i) dot = fmaf(dw[u * UV + i], r[i], dot);
+        float f = fmaf(2.0f, dot, e);
+        if (c == 0 || f < best) { best = f; bc = c; }
+      }
+      pick[u] = bc;
+      for (int j = u * UV; j < (u + 1) * UV; ++j) dwcur[j] = dwc[bc * 256 + j];
+    }
+  }
+  for (int u = 0; u < U; ++u) choices[u] = (uint8_t)pick[u];
+  free(dwc);
+  return st;
+}
+
+typedef struct {
+  int fmt;
+  const float *w, *grid, *imp, *hess;
+  int64_t rows, cols, rpe;
+  const int64_t *row_ids;
+  float perc_damp;
+  uint8_t *out;
+  int64_t r0, r1;
+  int st;
+} orc_cs_job;
+
+static void *choice_rows(void *p) {
+  orc_cs_job *J = (orc_cs_job *)p;
+  const orc_geom *G = &GEOM[J->fmt];
+  int64_t nb = J->cols / 256;
+  orc_scratch sc;
+  scratch_init(&sc, G->grid_n);
+  float ones[256];
+  for (int j = 0; j < 256; ++j) ones[j] = 1.0f;
+  for (int64_t i = J->r0; i < J->r1; ++i) {
+    int64_t r = J->row_ids ? J->row_ids[i] : i;
+    int64_t e = r / J->rpe;
+    for (int64_t b = 0; b < nb; ++b) {
+      const float *x = J->w + r * J->cols + b * 256;
+      const float *a = J->imp ? J->imp + e * J->cols + b * 256 : ones;
+      const float *H = J->hess + (e * nb + b) * 65536;
+      J->st |= choice_search_block(J->fmt, x, a, J->grid, H, J->perc_damp, J->out + (i * nb + b) * G->units, &sc);
+    }
+  }
+  scratch_free(&sc);
+  return NULL;
+}
+
+/* choices [n_rows, cols/256, units]; hess [E, cols/256, 256, 256] (row r uses
+ * expert r / rows_per_expert); importance as orc_quantize. */
+int orc_choice_search(int fmt, const float *w, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                      const int64_t *row_ids, int64_t n_rows, const float *grid, const float *imp,
+                      const float *hess, float perc_damp, uint8_t *out, int threads) {
+  if (fmt < 0 || fmt > 4 || cols % 256 != 0 || rows_per_expert <= 0) return -1;
+  int64_t n = row_ids ? n_rows : rows;
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  if (threads > n) threads = n > 0 ? (int)n : 1;
+  orc_cs_job jobs[256];
+  pthread_t th[256];
+  for (int i = 0; i < threads; ++i) {
+    orc_cs_job *J = &jobs[i];
+    J->fmt = fmt; J->w = w; J->grid = grid; J->imp = imp; J->hess = hess;
+    J->rows = rows; J->cols = cols; J->rpe = rows_per_expert; J->row_ids = row_ids;
+    J->perc_damp = perc_damp; J->out = out;
+    J->r0 = n * i / threads; J->r1 = n * (i + 1) / threads; J->st = 0;
+    pthread_create(&th[i], NULL, choice_rows, J);
+  }
+  int st = 0;
+  for (int i = 0; i < threads; ++i) { pthread_join(th[i], NULL); st |= jobs[i].st; }
+  return st;
+}
