@@ -31,6 +31,7 @@ SIGNATURES = {
     "iq_imatrix_importance": ([_P, _P, _I, _I64, _F, _P, _P, _P], _I),
     "iq_quantize": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
     "iq_quantize_every_choice": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "iq_choice_search": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _F, _P, _P, _P], _I),
     "iq_dequantize": ([_I, _P, _I64, _I64, _P, _P, _I, _P], _I),
     "iq_time_next_search": ([_P, _P], _I),
     "iq_error_string": ([_I], ctypes.c_char_p),
@@ -214,6 +215,37 @@ def quantize_every_choice(fmt, w: torch.Tensor, grid: torch.Tensor, importance: 
                                         _dev(out, "out", torch.uint8), _dev(status, "status", torch.int32),
                                         _stream())
     _check(rc, "iq_quantize_every_choice")
+    return out
+
+
+def choice_search(fmt, w: torch.Tensor, grid: torch.Tensor, hess: torch.Tensor,
+                  importance: torch.Tensor | None = None, rows_per_expert: int | None = None,
+                  perc_damp: float = 0.3, out: torch.Tensor | None = None,
+                  status: torch.Tensor | None = None) -> torch.Tensor:
+    """Local-Hessian choice search -> uint8 choices [rows, cols/256, choice_groups];
+    hess: [rows / rows_per_expert, cols/256, 256, 256] f32 diagonal Hessian blocks."""
+    f = _fmt(fmt)
+    if w.dim() != 2:
+        raise IQError("w must be [rows, cols]")
+    rows, cols = w.shape
+    info = format_info(f)
+    rpe = rows if rows_per_expert is None else int(rows_per_expert)
+    if tuple(grid.shape) != (info["grid_size"], 8):
+        raise IQError(f"grid must be [{info['grid_size']}, 8]")
+    if rpe < 1 or rows % rpe or tuple(hess.shape) != (rows // rpe, cols // 256, 256, 256):
+        raise IQError("hess must be [rows / rows_per_expert, cols/256, 256, 256]")
+    if importance is not None and (importance.dim() != 2 or importance.shape[1] != cols
+                                   or importance.shape[0] * rpe != rows):
+        raise IQError("importance must be [rows / rows_per_expert, cols]")
+    if out is None:
+        out = torch.empty((rows, cols // 256, info["choice_groups"]), dtype=torch.uint8, device=w.device)
+    if w.dtype not in DTYPE:
+        raise IQError(f"unsupported dtype {w.dtype}")
+    rc = lib().iq_choice_search(f, _dev(w, "w"), DTYPE[w.dtype], rows, cols, rpe, _dev(grid, "grid", torch.float32),
+                                _dev(importance, "importance", torch.float32), _dev(hess, "hess", torch.float32),
+                                float(perc_damp), _dev(out, "out", torch.uint8), _dev(status, "status", torch.int32),
+                                _stream())
+    _check(rc, "iq_choice_search")
     return out
 
 

@@ -118,6 +118,33 @@ int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, in
                          stream);
 }
 
+int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                     const float *grid, const float *importance, const float *hess, float perc_damp,
+                     uint8_t *choices, int32_t *status, hipStream_t stream) {
+  if (bad_fmt(fmt)) return IQ_ERR_FMT;
+  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
+  if (!w || !grid || !hess || !choices) return IQ_ERR_NULL;
+  if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
+  if (rows_per_expert < 1 || rows % rows_per_expert != 0) return IQ_ERR_SHAPE;
+  if (cols / 256 > (int64_t(1) << 24) || rows > (int64_t(1) << 40)) return IQ_ERR_SHAPE;
+  if (!(perc_damp >= 0.0f) || perc_damp > 3.0e38f) return IQ_ERR_ARG;
+  iq::EncArgs A{};
+  A.w = w;
+  A.dtype = dtype;
+  A.rows = rows;
+  A.cols = cols;
+  A.rpe = rows_per_expert;
+  A.E = rows / rows_per_expert;
+  A.nb = static_cast<int>(cols / 256);
+  A.grid = grid;
+  A.imp = importance;
+  A.status = status;
+  const int64_t wgg = (fmt == IQ_FMT_IQ1_M) ? 8 : 4;
+  const int64_t total = A.E * ((rows_per_expert + 63) / 64) * A.nb * (32 / wgg);
+  if (total >= (int64_t(1) << 31)) return IQ_ERR_SHAPE;
+  return iq::launch_choice_search(fmt, A, hess, perc_damp, choices, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
+}
+
 int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
                   int dtype, hipStream_t stream) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;

@@ -622,15 +622,10 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ld16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
 
+// Decode group g (0..31) of one block into 8 fp32 values.
 template <int F>
-__global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__ packed, int64_t ngroups,
-                                                      const float *__restrict__ grid, void *out, int dtype) {
+__device__ __forceinline__ void decode_group(const uint8_t *blk, int g, const float *__restrict__ grid, float y[8]) {
   using G = Geo<F>;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= ngroups) return;
-  const int64_t blkno = i >> 5;
-  const int g = static_cast<int>(i & 31);
-  const uint8_t *blk = packed + blkno * G::BYTES;
   uint32_t d16, k, mask = 0, h = 0, ls;
   const int u = g / G::GPU;
   if (F == IQ2_XXS) {
@@ -672,7 +667,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
     ls = (ld16(blk + 48 + 2 * (u >> 2)) >> (3 * (u & 3))) & 7u;
   }
   const float d = f16_bits_to_f32(static_cast<uint16_t>(d16));
-  float gv[8], y[8];
+  float gv[8];
   load_entry(grid + static_cast<int64_t>(k) * 8, gv);
   if (!G::IQ1) {
     const float s = d * (static_cast<float>(2 * ls + 1) * 0.125f);
@@ -687,6 +682,16 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = s * (gv[j] + delta);
   }
+}
+
+template <int F>
+__global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__ packed, int64_t ngroups,
+                                                      const float *__restrict__ grid, void *out, int dtype) {
+  using G = Geo<F>;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= ngroups) return;
+  float y[8];
+  decode_group<F>(packed + (i >> 5) * G::BYTES, static_cast<int>(i & 31), grid, y);
   if (dtype == 1) {
     uint4 o;
     o.x = f32_to_bf16(y[0]) | (static_cast<uint32_t>(f32_to_bf16(y[1])) << 16);
@@ -699,6 +704,129 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
     o[0] = make_float4(y[0], y[1], y[2], y[3]);
     o[1] = make_float4(y[4], y[5], y[6], y[7]);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Local-Hessian choice search (ModelOpt PR #3158's choice_search): from the
+// payloads of every choice, give each unit its best choice under its own
+// damped diagonal Hessian block, then revisit the units twice, each taking the
+// choice that most lowers the block error dw H dw^T with the others held.
+// Evaluation order (fp32, explicit fmaf): unit error e = sum_i dw_i (sum_j
+// H_ij dw_j), i and j ascending over the unit's columns; cross term r_i =
+// sum over the block's other columns j (ascending) of H_ij dw_j at the current
+// picks; a candidate scores fmaf(2, dw . r, e); first minimum wins.  The
+// damped block is H + lambda I, lambda = perc_damp * mean(diag H).
+// One wave per (expert, 64-row tile, block): lanes are rows, so every H_ij is
+// a wave-uniform scalar load shared by the 64 rows.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) damping_kernel(const float *__restrict__ hess, int64_t n, float perc_damp,
+                                                       float *__restrict__ lam) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float *H = hess + i * 65536;
+  double acc = 0.0;
+  for (int j = 0; j < 256; ++j) acc += static_cast<double>(H[j * 257]);
+  lam[i] = perc_damp * static_cast<float>(acc / 256.0);
+}
+
+template <int F>
+__device__ __forceinline__ void unit_residual(const EncArgs &A, const uint8_t *every, int64_t stride, int64_t r,
+                                              int b, int c, int u, float *dw) {
+  using G = Geo<F>;
+  const uint8_t *blk = every + c * stride + (r * A.nb + b) * G::BYTES;
+#pragma unroll
+  for (int gi = 0; gi < G::GPU; ++gi) {
+    const int g = u * G::GPU + gi;
+    float y[8], x[8];
+    decode_group<F>(blk, g, A.grid, y);
+    load8(A.w, A.dtype, r * A.cols + static_cast<int64_t>(b) * 256 + g * 8, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dw[gi * 8 + j] = x[j] - y[j];
+  }
+}
+
+template <int F>
+__global__ void __launch_bounds__(64) choice_search_kernel(EncArgs A, const uint8_t *__restrict__ every,
+                                                            int64_t stride, const float *__restrict__ hess,
+                                                            const float *__restrict__ lamv,
+                                                            uint8_t *__restrict__ choices) {
+  using G = Geo<F>;
+  constexpr int U = G::UNITS, UV = 8 * G::GPU, NC = G::NC;
+  __shared__ uint8_t s_pick[U][64];
+  const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
+  const int64_t tile = L % A.tiles_per_e;
+  const int64_t q = L / A.tiles_per_e;
+  const int b = static_cast<int>(q % A.nb);
+  const int64_t e = q / A.nb;
+  const int lane = threadIdx.x;
+  const int64_t rin = tile * 64 + lane;
+  const bool valid = rin < A.rpe;
+  const int64_t r = e * A.rpe + (valid ? rin : A.rpe - 1);
+  const float *H = hess + (e * A.nb + b) * 65536;
+  const float lam = lamv[e * A.nb + b];
+
+  // each unit's best choice under its own damped block
+  for (int u = 0; u < U; ++u) {
+    float best = 0.0f;
+    int bc = 0;
+    for (int c = 0; c < NC; ++c) {
+      float dw[UV];
+      unit_residual<F>(A, every, stride, r, b, c, u, dw);
+      float err = 0.0f;
+#pragma unroll
+      for (int i = 0; i < UV; ++i) {
+        const float *Hi = H + (u * UV + i) * 256 + u * UV;
+        float y = 0.0f;
+#pragma unroll
+        for (int j = 0; j < UV; ++j) y = __builtin_fmaf(j == i ? Hi[j] + lam : Hi[j], dw[j], y);
+        err = __builtin_fmaf(dw[i], y, err);
+      }
+      if (c == 0 || err < best) { best = err; bc = c; }
+    }
+    s_pick[u][lane] = static_cast<uint8_t>(bc);
+  }
+  // two passes: each unit takes the choice that most lowers the block error
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int u = 0; u < U; ++u) {
+      float rr[UV];
+#pragma unroll
+      for (int i = 0; i < UV; ++i) rr[i] = 0.0f;
+      for (int v = 0; v < U; ++v) {
+        if (v == u) continue;
+        float dv[UV];
+        unit_residual<F>(A, every, stride, r, b, s_pick[v][lane], v, dv);
+#pragma unroll
+        for (int i = 0; i < UV; ++i) {
+          const float *Hi = H + (u * UV + i) * 256 + v * UV;
+#pragma unroll
+          for (int j = 0; j < UV; ++j) rr[i] = __builtin_fmaf(Hi[j], dv[j], rr[i]);
+        }
+      }
+      float best = 0.0f;
+      int bc = 0;
+      for (int c = 0; c < NC; ++c) {
+        float dw[UV];
+        unit_residual<F>(A, every, stride, r, b, c, u, dw);
+        float err = 0.0f, dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UV; ++i) {
+          const float *Hi = H + (u * UV + i) * 256 + u * UV;
+          float y = 0.0f;
+#pragma unroll
+          for (int j = 0; j < UV; ++j) y = __builtin_fmaf(j == i ? Hi[j] + lam : Hi[j], dw[j], y);
+          err = __builtin_fmaf(dw[i], y, err);
+        }
+#pragma unroll
+        for (int i = 0; i < UV; ++i) dot = __builtin_fmaf(dw[i], rr[i], dot);
+        const float f = __builtin_fmaf(2.0f, dot, err);
+        if (c == 0 || f < best) { best = f; bc = c; }
+      }
+      s_pick[u][lane] = static_cast<uint8_t>(bc);
+    }
+  }
+  if (!valid) return;
+#pragma unroll
+  for (int u = 0; u < U; ++u) choices[(r * A.nb + b) * U + u] = s_pick[u][lane];
 }
 
 // ---------------------------------------------------------------------------
@@ -782,6 +910,49 @@ int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, co
     case IQ2_S: return launch_decode_t<IQ2_S>(packed, rows, cols, grid, out, dtype, stream);
     case IQ1_S: return launch_decode_t<IQ1_S>(packed, rows, cols, grid, out, dtype, stream);
     case IQ1_M: return launch_decode_t<IQ1_M>(packed, rows, cols, grid, out, dtype, stream);
+  }
+  return -1;
+}
+
+template <int F>
+static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp, uint8_t *choices,
+                                  hipStream_t stream) {
+  using G = Geo<F>;
+  const int64_t nblocks = A.rows * A.nb;
+  if (nblocks == 0) return 0;
+  const size_t pbytes = static_cast<size_t>(G::NC) * nblocks * G::BYTES;
+  const int64_t nl = A.E * A.nb;
+  void *scratch = nullptr;
+  if (hipMallocAsync(&scratch, ((pbytes + 255) & ~size_t(255)) + nl * sizeof(float), stream) != hipSuccess)
+    return -1;
+  uint8_t *every = static_cast<uint8_t *>(scratch);
+  float *lam = reinterpret_cast<float *>(static_cast<char *>(scratch) + ((pbytes + 255) & ~size_t(255)));
+  EncArgs E = A;
+  E.out = every;
+  E.choices = nullptr;
+  E.copies = G::NC;
+  E.copy_stride = nblocks * G::BYTES;
+  int rc = launch_quantize_t<F>(E, true, stream);
+  hipLaunchKernelGGL(damping_kernel, dim3(static_cast<unsigned>((nl + 255) / 256)), dim3(256), 0, stream, hess, nl,
+                     perc_damp, lam);
+  A.tiles_per_e = (A.rpe + 63) / 64;
+  A.total_wg = A.E * A.tiles_per_e * A.nb;
+  hipLaunchKernelGGL(choice_search_kernel<F>, dim3(static_cast<unsigned>(A.total_wg)), dim3(64), 0, stream, A,
+                     static_cast<const uint8_t *>(every), E.copy_stride, hess, static_cast<const float *>(lam),
+                     choices);
+  const hipError_t le = hipGetLastError();
+  hipFreeAsync(scratch, stream);
+  return (rc == 0 && le == hipSuccess) ? 0 : -1;
+}
+
+int launch_choice_search(int fmt, EncArgs A, const float *hess, float perc_damp, uint8_t *choices,
+                         hipStream_t stream) {
+  switch (fmt) {
+    case IQ2_XXS: return launch_choice_search_t<IQ2_XXS>(A, hess, perc_damp, choices, stream);
+    case IQ2_XS: return launch_choice_search_t<IQ2_XS>(A, hess, perc_damp, choices, stream);
+    case IQ2_S: return launch_choice_search_t<IQ2_S>(A, hess, perc_damp, choices, stream);
+    case IQ1_S: return launch_choice_search_t<IQ1_S>(A, hess, perc_damp, choices, stream);
+    case IQ1_M: return launch_choice_search_t<IQ1_M>(A, hess, perc_damp, choices, stream);
   }
   return -1;
 }

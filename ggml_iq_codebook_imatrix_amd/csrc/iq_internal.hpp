@@ -29,6 +29,8 @@ struct EncArgs {
 void take_search_events(hipEvent_t *start, hipEvent_t *stop);
 
 int launch_quantize(int fmt, EncArgs A, bool every_choice, hipStream_t stream);
+int launch_choice_search(int fmt, EncArgs A, const float *hess, float perc_damp, uint8_t *choices,
+                         hipStream_t stream);
 int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
                   int dtype, hipStream_t stream);
 int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,

@@ -23,7 +23,8 @@
  *             MoE experts" (ModelOpt PR), description.
  *  [2513]     ModelOpt PR #2513: IQ2_XXS / IQ2_S / IQ1_M commit messages, IQ1_M body.
  *  [3157]     "[1/5] Let the GGML IQ encoders take fixed per-group choices"
- *             (ModelOpt PR), description and review.
+ *             (ModelOpt PR), description and review, and the squashed follow-ups
+ *             on that page (#3158 local_hessian, #3159 every-choice encode).
  *  [recipes]  modelopt_recipes folder page, IQ1_M CUDA encoder commit.
  *  [coverage] "MoE expert coverage in imatrix calibration", Facts.
  */
@@ -165,6 +166,25 @@ int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
 int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
                              int64_t rows_per_expert, const float *grid, const float *importance,
                              uint8_t *out, int32_t *status, hipStream_t stream);
+
+/* Local-Hessian choice search ([3157] series, squashed #3158 "local_hessian
+ * for GGML IQ": encode each block under every choice; give each choice unit its
+ * best choice under its own block of the damped input Hessian; revisit the units
+ * twice, each taking the choice that most lowers the block's layer-output error
+ * dw H dw^T with the others held; blocks damped by perc_damp as GPTQ damps).
+ *  hess     (device) [rows / rows_per_expert, cols/256, 256, 256] f32: the
+ *           256-column diagonal blocks of each expert's input Hessian X^T X.
+ *  perc_damp  H_b + perc_damp * mean(diag H_b) * I is used (0.3 in [3158]).
+ *  choices  (device) [rows, cols/256, choice_groups] uint8 OUT: the picks, to be
+ *           passed to iq_quantize (IQ1_S: (delta_sign << 3) | local scale).
+ *  importance, grid, w, rows_per_expert, status: as iq_quantize (the codebook
+ *  search keeps the importance weighting).
+ * Errors: as iq_quantize, plus IQ_ERR_NULL (hess, choices) and IQ_ERR_ARG
+ * (perc_damp negative or not finite). */
+int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
+                     int64_t rows_per_expert, const float *grid, const float *importance,
+                     const float *hess, float perc_damp, uint8_t *choices, int32_t *status,
+                     hipStream_t stream);
 
 /* Decode ([2513]: dequantize_row semantics; IQ1_M d reassembled from the top
  * nibbles of the four scale words, one 3-bit scale per two groups).

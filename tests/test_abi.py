@@ -32,7 +32,8 @@ def api():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["iq_format_info", "iq_imatrix_collect", "iq_imatrix_importance", "iq_quantize",
-         "iq_quantize_every_choice", "iq_dequantize", "iq_time_next_search", "iq_error_string"])
+         "iq_quantize_every_choice", "iq_choice_search", "iq_dequantize", "iq_time_next_search",
+         "iq_error_string"])
 
 
 def test_library_exports_every_declared_symbol(api):
@@ -69,6 +70,10 @@ def test_host_validation_quantize(api):
     ev = lambda fmt=0, cols=512, out=FAKE: L.iq_quantize_every_choice(fmt, FAKE, 1, 64, cols, 64, FAKE, None, out,
                                                                       None, None)
     assert ev(fmt=7) == -1 and ev(cols=100) == -4 and ev(out=None) == -3
+    cs = lambda fmt=0, hess=FAKE, ch=FAKE, damp=0.3, rpe=64: L.iq_choice_search(fmt, FAKE, 1, 64, 512, rpe, FAKE, None,
+                                                                              hess, damp, ch, None, None)
+    assert cs(fmt=9) == -1 and cs(hess=None) == -3 and cs(ch=None) == -3 and cs(rpe=7) == -4
+    assert cs(damp=-1.0) == -5 and cs(damp=float("inf")) == -5
     assert L.iq_format_info(0, None) == -3
     assert api.lib().iq_error_string(-4) == b"invalid shape"
     assert L.iq_time_next_search(FAKE, None) == -3 and L.iq_time_next_search(None, FAKE) == -3

@@ -169,6 +169,45 @@ def test_every_choice_full_size_sampled(api, orc):
     assert np.array_equal(every[:, rid], want)
 
 
+def _correlated_hessian(E, nb, T, seed):
+    """[E, nb, 256, 256] f32 diagonal blocks of X^T X from banded-correlated tokens."""
+    g = inputs.rng(seed)
+    out = np.empty((E, nb, 256, 256), np.float32)
+    band = (np.abs(np.arange(256)[:, None] - np.arange(256)[None, :]) < 6)
+    for e in range(E):
+        for b in range(nb):
+            z = g.standard_normal((T, 256)).astype(np.float32)
+            mix = (np.eye(256) + 0.4 * g.standard_normal((256, 256)) * band).astype(np.float32)
+            x = z @ mix
+            out[e, b] = (x.T.astype(np.float64) @ x).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_choice_search_parity(api, orc, fmt):
+    """Local-Hessian choice search (ModelOpt PR #3158) against the oracle: picks
+    bit-exact; experts with ragged 64-row tiles and an identity Hessian expert."""
+    say("choice search", fmt)
+    grid = inputs.grid_for(fmt, GRID_SEED[fmt])
+    rows, cols, rpe = 2 * 70, 512, 70
+    w = inputs.weight(rows, cols, 2300, 2301)
+    hess = _correlated_hessian(2, 2, 300, 2302)
+    hess[1, 1] = np.eye(256, dtype=np.float32) * np.float32(7.0)
+    imp = np.sqrt(np.stack([np.concatenate([np.diag(hess[e, b]) for b in range(2)]) for e in range(2)]) / 300)
+    imp = imp.astype(np.float32)
+    st = api.new_status()
+    got = host(api.choice_search(fmt, dev_w(w, "bf16"), dev(grid), dev(hess), dev(imp), rows_per_expert=rpe,
+                                 perc_damp=0.3, status=st))
+    assert int(host(st)[0]) == 0
+    want, _ = orc.choice_search(fmt, w, grid, hess, imp, rows_per_expert=rpe, perc_damp=0.3)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} picks differ, first {bad[:5].tolist()}"
+    # the picks feed the fixed-choice encoder
+    p = host(api.quantize(fmt, dev_w(w, "bf16"), dev(grid), dev(imp), rows_per_expert=rpe, choices=dev(got)))
+    pw, _ = orc.quantize(fmt, w, grid, imp, rows_per_expert=rpe, choices=want)
+    assert np.array_equal(p, pw)
+
+
 def test_encode_is_deterministic(api):
     say("determinism")
     fmt = "IQ2_S"
