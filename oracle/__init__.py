@@ -52,6 +52,7 @@ def lib():
         L.orc_f16_to_f32.restype = ctypes.c_float
         L.orc_collect.argtypes = [P, i64, i64, P, ci, ci, P, P]
         L.orc_importance.argtypes = [P, P, ci, i64, ctypes.c_float, P]
+        L.orc_hessian_collect.argtypes = [P, i64, i64, P, ci, ci, P]
         L.orc_fixed_mean.argtypes = [P, i64]
         L.orc_fixed_mean.restype = ctypes.c_float
         L.orc_anchor.argtypes = [ci, P, P]
@@ -112,6 +113,20 @@ def collect(x, ids=None, num_experts: int = 1, sums=None, counts=None):
         top_k = ids.shape[1]
     st = lib().orc_collect(_p(x), T, K, _p(ids), top_k, E, _p(sums), _p(counts))
     return sums, counts, st
+
+
+def hessian_collect(x, ids=None, num_experts: int = 1, hess=None):
+    """fp64 [E, K/256, 256, 256] diagonal blocks of each expert's X^T X (accumulated)."""
+    x = _f32(x)
+    T, K = x.shape
+    E = 1 if ids is None else int(num_experts)
+    hess = np.zeros((E, K // 256, 256, 256), dtype=np.float64) if hess is None else hess
+    top_k = 0
+    if ids is not None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        top_k = ids.shape[1]
+    st = lib().orc_hessian_collect(_p(x), T, K, _p(ids), top_k, E, _p(hess))
+    return hess, st
 
 
 def importance(sums32, counts, floor_rel: float = 1e-6):

@@ -161,6 +161,32 @@ int orc_collect(const float *x, int64_t T, int64_t K, const int32_t *ids, int to
   return st;
 }
 
+/* Hessian blocks for the local-Hessian choice search ([3158]: the layer-output
+ * error over the 256-column diagonal blocks of the input Hessian X^T X).
+ * hess [E][K/256][256][256] fp64, accumulated in place: for each (t, s) with
+ * ids[t][s] == e (dense: every token, E = 1), add x_t,b x_t,b^T to block b. */
+int orc_hessian_collect(const float *x, int64_t T, int64_t K, const int32_t *ids, int top_k, int num_experts,
+                        double *hess) {
+  int st = 0;
+  int64_t nb = K / 256;
+  for (int64_t t = 0; t < T; ++t) {
+    int ns = ids ? top_k : 1;
+    for (int s = 0; s < ns; ++s) {
+      int e = ids ? ids[t * top_k + s] : 0;
+      if (e < 0 || e >= num_experts) { st |= ORC_ST_BADID; continue; }
+      for (int64_t b = 0; b < nb; ++b) {
+        const float *xb = x + t * K + b * 256;
+        double *H = hess + ((int64_t)e * nb + b) * 65536;
+        for (int i = 0; i < 256; ++i) {
+          if (!isfinite(xb[i])) st |= ORC_ST_NONFINITE;
+          for (int j = 0; j < 256; ++j) H[i * 256 + j] += (double)xb[i] * (double)xb[j];
+        }
+      }
+    }
+  }
+  return st;
+}
+
 /* Importance a_j = sqrt(floored E[x_j^2]) per expert  ([2735] "What imatrix
  * does", "Why the square root", "Shared floor"; [coverage] Facts: count 0 ->
  * weight 1 on every channel).  sums are the fp32 statistics.  R6.

@@ -162,6 +162,33 @@ def test_collect_moe_histogram_and_sums(orc):
     assert c2[1] == np.bincount(ids2.ravel(), minlength=E)[1]
 
 
+def test_hessian_blocks_pinned_by_collector_and_outer_products(orc):
+    """Diagonal of each block = the imatrix collector's per-column sum of squares
+    (exact in fp64 for bf16 inputs); blocks symmetric; a brute-force sum of
+    outer products over the routed (token, slot) pairs matches."""
+    T, K, E, top_k = 40, 512, 5, 2
+    x = inputs.activations(T, K, 3500, 3501, bf16=True)
+    ids = inputs.routing(T, top_k, E, 3502, n_idle=1)
+    ids[2] = [3, 3]
+    H, st = orc.hessian_collect(x, ids, E)
+    sums, counts, _ = orc.collect(x, ids, E)
+    assert st == 0
+    for e in range(E):
+        for b in range(2):
+            assert np.array_equal(np.diag(H[e, b]), sums[e, 256 * b:256 * (b + 1)])
+            assert np.array_equal(H[e, b], H[e, b].T)
+    e, b = 3, 1
+    ref = np.zeros((256, 256))
+    for t in range(T):
+        for s in range(top_k):
+            if ids[t, s] == e:
+                v = x[t, 256 * b:256 * (b + 1)].astype(np.float64)
+                ref += np.outer(v, v)
+    assert np.allclose(H[e, b], ref, rtol=1e-13, atol=0)
+    Hd, _ = orc.hessian_collect(x)
+    assert np.allclose(np.diag(Hd[0, 0]), np.square(x[:, :256].astype(np.float64)).sum(0), rtol=1e-14)
+
+
 def test_collect_flags_nonfinite_and_bad_ids(orc):
     x = np.ones((4, 8), np.float32)
     x[2, 3] = np.inf
