@@ -28,6 +28,7 @@ _P, _I, _I64, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
 SIGNATURES = {
     "iq_format_info": ([_I, _P], _I),
     "iq_imatrix_collect": ([_P, _I, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P], _I),
+    "iq_hessian_collect": ([_P, _I, _I64, _I64, _P, _I, _I, _I, _P, _P, _P], _I),
     "iq_imatrix_importance": ([_P, _P, _I, _I64, _F, _P, _P, _P], _I),
     "iq_quantize": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
     "iq_quantize_every_choice": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P], _I),
@@ -136,6 +137,34 @@ def imatrix_collect(x: torch.Tensor, ids: torch.Tensor | None = None, num_expert
                                   _stream())
     _check(rc, "iq_imatrix_collect")
     return sums, counts
+
+
+def hessian_collect(x: torch.Tensor, ids: torch.Tensor | None = None, num_experts: int = 1,
+                    chunk_rows: int = 1024, hess: torch.Tensor | None = None,
+                    status: torch.Tensor | None = None) -> torch.Tensor:
+    """Accumulate each expert's 256-column diagonal blocks of X^T X -> hess [E, K/256, 256, 256] f32."""
+    if x.dim() != 2:
+        raise IQError("x must be [T, K]")
+    T, K = x.shape
+    E = int(num_experts)
+    if K % 256:
+        raise IQError("K must be a multiple of 256")
+    if hess is None:
+        hess = torch.zeros((E, K // 256, 256, 256), dtype=torch.float32, device=x.device)
+    top_k = 0
+    if ids is not None:
+        if ids.dim() != 2 or ids.shape[0] != T:
+            raise IQError("ids must be [T, top_k]")
+        top_k = ids.shape[1]
+    if tuple(hess.shape) != (E, K // 256, 256, 256):
+        raise IQError("hess must be [E, K/256, 256, 256]")
+    if x.dtype not in DTYPE:
+        raise IQError(f"unsupported dtype {x.dtype}")
+    rc = lib().iq_hessian_collect(_dev(x, "x"), DTYPE[x.dtype], T, K, _dev(ids, "ids", torch.int32), top_k, E,
+                                  int(chunk_rows), _dev(hess, "hess", torch.float32),
+                                  _dev(status, "status", torch.int32), _stream())
+    _check(rc, "iq_hessian_collect")
+    return hess
 
 
 def imatrix_importance(sums: torch.Tensor, counts: torch.Tensor, floor_rel: float = 1e-6,

@@ -64,6 +64,20 @@ int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int
              : IQ_ERR_HIP;
 }
 
+int iq_hessian_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
+                       int num_experts, int chunk_rows, float *hess, int32_t *status, hipStream_t stream) {
+  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
+  if (!x || !hess) return IQ_ERR_NULL;
+  if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1) return IQ_ERR_ARG;
+  if (ids && top_k < 1) return IQ_ERR_ARG;
+  if (!ids && num_experts != 1) return IQ_ERR_ARG;
+  if (K % 256 != 0) return IQ_ERR_SHAPE;
+  if (static_cast<int64_t>(num_experts) * K > (int64_t(1) << 30) || T > (int64_t(1) << 31) - 1) return IQ_ERR_ARG;
+  return iq::launch_hessian(x, dtype, T, K, ids, ids ? top_k : 0, num_experts, chunk_rows, hess, status, stream) == 0
+             ? IQ_OK
+             : IQ_ERR_HIP;
+}
+
 int iq_imatrix_importance(const float *sums, const int64_t *counts, int num_experts, int64_t K, float floor_rel,
                           float *importance, int32_t *status, hipStream_t stream) {
   if (!sums || !counts || !importance) return IQ_ERR_NULL;

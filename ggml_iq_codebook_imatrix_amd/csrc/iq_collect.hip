@@ -20,6 +20,8 @@
 // running sums in chunk order.  The sums therefore repeat bit for bit, and no
 // x^2 temporary of the activation's size is ever materialised.
 
+#include <type_traits>
+
 #include "iq_common.hpp"
 #include "iq_internal.hpp"
 
@@ -285,6 +287,277 @@ int launch_importance(const float *sums, const int64_t *counts, int E, int64_t K
   hipLaunchKernelGGL(importance_kernel, dim3(static_cast<unsigned>(E)), dim3(1024), 0, stream, sums, counts, K,
                      floor_rel, L, imp, status);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Hessian diagonal blocks for the local-Hessian choice search (ModelOpt PR
+// #3158: the layer-output error is taken over the 256-column diagonal blocks
+// of the input Hessian).  hess[e][b] += sum over the (token, slot) pairs
+// routed to e of x_t,b x_t,b^T, x_t,b the token's 256 columns of block b.
+//
+// A dense contraction, so it runs on the matrix cores.  One wave computes one
+// 64x64 tile (ti <= tj of the 4x4 tiles of a block; the mirror tile is written
+// from the same registers, so the result is exactly symmetric) as 2x2 MFMA
+// 32x32 tiles (bf16: v_mfma_f32_32x32x16_bf16, whose products are exact in
+// fp32; f32: v_mfma_f32_32x32x2_f32) over one token range.  Each step stages
+// 32 tokens transposed in LDS ([column][token], padded rows), the operand
+// layout the MFMA reads.  Tokens are taken in ascending order, each as often
+// as it is routed to e; token ranges ("splits") give the chip enough waves
+// when E * blocks is small, and their partial tiles are added in split order,
+// so the sums repeat bit for bit.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kHTok = 32;  // tokens per step
+
+template <int DT>
+__global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x, int64_t T, int64_t K,
+                                                     const int32_t *__restrict__ ids, int top_k, int E,
+                                                     int chunk_rows, int W, const uint32_t *__restrict__ bm,
+                                                     int64_t split_len, float *__restrict__ dst, bool accumulate,
+                                                     int32_t *status) {
+  constexpr int RS = DT == 1 ? 40 : 33;  // LDS row: 32 tokens + padding (bf16 80 B, f32 132 B)
+  using elem_t = typename std::conditional<DT == 1, uint16_t, float>::type;
+  __shared__ __attribute__((aligned(16))) elem_t sA[64][RS];
+  __shared__ __attribute__((aligned(16))) elem_t sB[64][RS];
+  __shared__ int s_tok[kHTok];
+  const int64_t nb = K / 256;
+  const int64_t ntiles = static_cast<int64_t>(E) * nb * 10;
+  const int64_t split = blockIdx.x / ntiles;
+  const int64_t rem = blockIdx.x % ntiles;
+  int tp = static_cast<int>(rem % 10);
+  const int64_t eb = rem / 10;
+  const int b = static_cast<int>(eb % nb);
+  const int e = static_cast<int>(eb / nb);
+  int ti = 0;
+  while (tp >= 4 - ti) { tp -= 4 - ti; ++ti; }
+  const int tj = ti + tp;
+  const int lane = threadIdx.x;
+  const int64_t colA = static_cast<int64_t>(b) * 256 + ti * 64, colB = static_cast<int64_t>(b) * 256 + tj * 64;
+  const int64_t t0 = split * split_len;
+  const int64_t t1 = (t0 + split_len < T) ? t0 + split_len : T;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  // routed token stream, advanced by lane 0 only: the word being read (its
+  // remaining bits and the token of bit 0), the next token to read a word at,
+  // and the repeats still owed to the last token taken
+  int64_t tw = t0, wbase = 0, last = 0;
+  uint32_t bits = 0u;
+  int pending = 0;
+  int64_t cur = t0;  // dense stream
+  bool finite = true;
+  while (true) {
+    int nt = 0;
+    if (ids == nullptr) {
+      nt = static_cast<int>((t1 - cur < kHTok) ? t1 - cur : kHTok);
+      if (lane < kHTok) s_tok[lane] = lane < nt ? static_cast<int>(cur + lane) : -1;
+      cur += nt;
+    } else {
+      if (lane == 0) {
+        while (nt < kHTok) {
+          if (pending > 0) {
+            s_tok[nt++] = static_cast<int>(last);
+            --pending;
+            continue;
+          }
+          if (bits == 0u) {
+            if (tw >= t1) break;
+            const int64_t ch = tw / chunk_rows, p = tw - ch * chunk_rows;
+            const int sh = static_cast<int>(p & 31);
+            wbase = tw - sh;
+            bits = (bm[(ch * E + e) * W + (p >> 5)] >> sh) << sh;
+            int64_t next = ch * chunk_rows + (p | 31) + 1;
+            if (next > (ch + 1) * chunk_rows) next = (ch + 1) * chunk_rows;
+            if (next > t1) next = t1;
+            if (next - wbase < 32) bits &= (1u << (next - wbase)) - 1u;
+            tw = next;
+            continue;
+          }
+          last = wbase + __builtin_ctz(bits);
+          bits &= bits - 1u;
+          int mult = 0;
+          for (int s = 0; s < top_k; ++s) mult += ids[last * top_k + s] == e;
+          s_tok[nt++] = static_cast<int>(last);
+          pending = mult - 1;
+        }
+        for (int q = nt; q < kHTok; ++q) s_tok[q] = -1;
+      }
+      nt = __shfl(nt, 0);
+    }
+    __syncthreads();
+    if (nt == 0) break;
+    if (DT == 1) {
+      // lane: column pair cp (columns 2cp, 2cp+1 of the tile), token octets tg, tg + 2
+      const int cp = lane & 31;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int g = (lane >> 5) + 2 * it;
+        uint32_t va[8], vb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int tok = s_tok[8 * g + j];
+          va[j] = 0u;
+          vb[j] = 0u;
+          if (tok >= 0) {
+            const uint16_t *xr = static_cast<const uint16_t *>(x) + static_cast<int64_t>(tok) * K;
+            va[j] = *reinterpret_cast<const uint32_t *>(xr + colA + 2 * cp);
+            vb[j] = *reinterpret_cast<const uint32_t *>(xr + colB + 2 * cp);
+          }
+        }
+        uint4 a0, a1, b0, b1;
+        uint32_t *pa0 = &a0.x, *pa1 = &a1.x, *pb0 = &b0.x, *pb1 = &b1.x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pa0[j] = (va[2 * j] & 0xffffu) | (va[2 * j + 1] << 16);
+          pa1[j] = (va[2 * j] >> 16) | (va[2 * j + 1] & 0xffff0000u);
+          pb0[j] = (vb[2 * j] & 0xffffu) | (vb[2 * j + 1] << 16);
+          pb1[j] = (vb[2 * j] >> 16) | (vb[2 * j + 1] & 0xffff0000u);
+          finite = finite && finite_f(__uint_as_float(va[2 * j] << 16)) &&
+                   finite_f(__uint_as_float(va[2 * j] & 0xffff0000u)) &&
+                   finite_f(__uint_as_float(va[2 * j + 1] << 16)) &&
+                   finite_f(__uint_as_float(va[2 * j + 1] & 0xffff0000u));
+        }
+        *reinterpret_cast<uint4 *>(&sA[2 * cp][8 * g]) = a0;
+        *reinterpret_cast<uint4 *>(&sA[2 * cp + 1][8 * g]) = a1;
+        *reinterpret_cast<uint4 *>(&sB[2 * cp][8 * g]) = b0;
+        *reinterpret_cast<uint4 *>(&sB[2 * cp + 1][8 * g]) = b1;
+      }
+    } else {
+      // lane: 4 columns cc..cc+3 of one token per iteration
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int qd = lane + 64 * it;
+        const int tt = qd >> 4, cc = (qd & 15) * 4;
+        const int tok = s_tok[tt];
+        float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tok >= 0) {
+          const float *xr = static_cast<const float *>(x) + static_cast<int64_t>(tok) * K;
+          va = *reinterpret_cast<const float4 *>(xr + colA + cc);
+          vb = *reinterpret_cast<const float4 *>(xr + colB + cc);
+        }
+        sA[cc][tt] = va.x; sA[cc + 1][tt] = va.y; sA[cc + 2][tt] = va.z; sA[cc + 3][tt] = va.w;
+        sB[cc][tt] = vb.x; sB[cc + 1][tt] = vb.y; sB[cc + 2][tt] = vb.z; sB[cc + 3][tt] = vb.w;
+        finite = finite && finite_f(va.x) && finite_f(va.y) && finite_f(va.z) && finite_f(va.w);
+      }
+    }
+    __syncthreads();
+    if (DT == 1) {
+#pragma unroll
+      for (int ks = 0; ks < kHTok / 16; ++ks) {
+        bf16x8_t a[2], bb[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          a[m] = *reinterpret_cast<const bf16x8_t *>(&sA[m * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+          bb[m] = *reinterpret_cast<const bf16x8_t *>(&sB[m * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bb[n], acc[m][n], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kHTok / 2; ++ks) {
+        float a[2], bb[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          a[m] = sA[m * 32 + (lane & 31)][2 * ks + (lane >> 5)];
+          bb[m] = sB[m * 32 + (lane & 31)][2 * ks + (lane >> 5)];
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], bb[n], acc[m][n], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  if (!finite) raise_status(status, ST_NONFINITE);
+  // dst: hess itself (one split, accumulate) or this split's partial blocks
+  float *Hb = dst + ((split * E + e) * nb + b) * 65536;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = ti * 64 + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int col = tj * 64 + n * 32 + (lane & 31);
+        const float v = acc[m][n][q];
+        if (accumulate) {
+          Hb[row * 256 + col] += v;
+          if (ti != tj) Hb[col * 256 + row] += v;
+        } else {
+          Hb[row * 256 + col] = v;
+          if (ti != tj) Hb[col * 256 + row] = v;
+        }
+      }
+}
+
+// hess[i] += partial[0][i] + partial[1][i] + ... in split order.
+__global__ void __launch_bounds__(256) hessian_combine_kernel(const float *__restrict__ partial, int64_t nsplit,
+                                                              int64_t n, float *__restrict__ hess) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = partial[i];
+  for (int64_t k = 1; k < nsplit; ++k) s = s + partial[k * n + i];
+  hess[i] = hess[i] + s;
+}
+
+int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
+                   int chunk_rows, float *hess, int32_t *status, hipStream_t stream) {
+  if (T == 0) return 0;
+  const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
+  const int W = (chunk_rows + 31) / 32 + 1;
+  const int64_t ntiles = static_cast<int64_t>(E) * (K / 256) * 10;
+  // enough waves for 256 CUs, with at least 256 tokens per split
+  int64_t nsplit = 1;
+  if (ntiles < 2048) {
+    nsplit = (2048 + ntiles - 1) / ntiles;
+    const int64_t by_tokens = (T + 255) / 256;
+    if (nsplit > by_tokens) nsplit = by_tokens;
+    if (nsplit < 1) nsplit = 1;
+  }
+  const int64_t split_len = ((T + nsplit - 1) / nsplit + kHTok - 1) / kHTok * kHTok;
+  nsplit = (T + split_len - 1) / split_len;
+  const int64_t hn = static_cast<int64_t>(E) * (K / 256) * 65536;
+  const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
+  const size_t cbytes = ids ? static_cast<size_t>(E) * sizeof(int64_t) : 0;
+  const size_t pbytes = nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0;
+  void *scratch = nullptr;
+  const size_t off_b = (pbytes + 255) & ~size_t(255), off_c = off_b + ((bbytes + 255) & ~size_t(255));
+  if (off_c + cbytes > 0 && hipMallocAsync(&scratch, off_c + cbytes + 256, stream) != hipSuccess) return -1;
+  float *partial = static_cast<float *>(scratch);
+  uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + off_b) : nullptr;
+  int64_t *cnt = ids ? reinterpret_cast<int64_t *>(static_cast<char *>(scratch) + off_c) : nullptr;
+  if (ids)
+    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks)), dim3(256), 0, stream, ids, T,
+                       top_k, E, chunk_rows, W, bm, cnt, status);
+  float *dst = nsplit > 1 ? partial : hess;
+  const bool accumulate = nsplit == 1;
+  const dim3 g(static_cast<unsigned>(ntiles * nsplit));
+  if (dtype == 1)
+    hipLaunchKernelGGL(hessian_kernel<1>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E, chunk_rows, W,
+                       static_cast<const uint32_t *>(bm), split_len, dst, accumulate, status);
+  else
+    hipLaunchKernelGGL(hessian_kernel<0>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E, chunk_rows, W,
+                       static_cast<const uint32_t *>(bm), split_len, dst, accumulate, status);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(hessian_combine_kernel, dim3(static_cast<unsigned>((hn + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float *>(partial), nsplit, hn, hess);
+  const hipError_t le = hipGetLastError();
+  if (scratch) hipFreeAsync(scratch, stream);
+  return le == hipSuccess ? 0 : -1;
 }
 
 }  // namespace iq

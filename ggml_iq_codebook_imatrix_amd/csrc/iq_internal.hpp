@@ -35,6 +35,8 @@ int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, co
                   int dtype, hipStream_t stream);
 int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
                    int chunk_rows, float *sums, int64_t *counts, int32_t *status, hipStream_t stream);
+int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
+                   int chunk_rows, float *hess, int32_t *status, hipStream_t stream);
 int launch_importance(const float *sums, const int64_t *counts, int E, int64_t K, float floor_rel,
                       float *imp, int32_t *status, hipStream_t stream);
 

@@ -186,6 +186,26 @@ int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t co
                      const float *hess, float perc_damp, uint8_t *choices, int32_t *status,
                      hipStream_t stream);
 
+/* Hessian diagonal blocks for iq_choice_search ([3157] series, squashed #3158
+ * "local_hessian for GGML IQ": the layer-output error is measured under the
+ * 256-column diagonal blocks of each weight's input Hessian X^T X, gathered
+ * from the same calibration tokens as the imatrix, routed per expert).
+ *  x, dtype, T, K, ids, top_k, num_experts, chunk_rows: as iq_imatrix_collect;
+ *           K must be a multiple of 256.
+ *  hess     (device) [num_experts, K/256, 256, 256] f32, ACCUMULATED:
+ *           hess[e][b][i][j] += sum over the (t, s) pairs with ids[t][s] == e of
+ *           x[t][256b + i] * x[t][256b + j] (dense: every token, e = 0).  Each
+ *           block is exactly symmetric.  Tokens are added in ascending order in
+ *           fixed token ranges, so results repeat bit for bit.
+ *  status   (device, nullable): IQ_STATUS_NONFINITE when a token that reached an
+ *           expert holds a non-finite value; IQ_STATUS_BADID as
+ *           iq_imatrix_collect.
+ * Errors: as iq_imatrix_collect, plus IQ_ERR_NULL (hess), IQ_ERR_SHAPE (K not a
+ * multiple of 256) and IQ_ERR_ARG (num_experts * K above 2^30, T of 2^31 or
+ * more). */
+int iq_hessian_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
+                       int num_experts, int chunk_rows, float *hess, int32_t *status, hipStream_t stream);
+
 /* Decode ([2513]: dequantize_row semantics; IQ1_M d reassembled from the top
  * nibbles of the four scale words, one 3-bit scale per two groups).
  *  packed (device) [rows, cols/256, block_bytes]; grid (device) [grid_size, 8];

@@ -31,7 +31,7 @@ def api():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["iq_format_info", "iq_imatrix_collect", "iq_imatrix_importance", "iq_quantize",
+        ["iq_format_info", "iq_imatrix_collect", "iq_hessian_collect", "iq_imatrix_importance", "iq_quantize",
          "iq_quantize_every_choice", "iq_choice_search", "iq_dequantize", "iq_time_next_search",
          "iq_error_string"])
 
@@ -89,6 +89,12 @@ def test_host_validation_collect_importance_decode(api):
     assert c(T=-1) == -5 and c(K=0) == -5 and c(chunk=0) == -5 and c(E=0) == -5
     assert c(E=4) == -5                           # dense needs one statistic
     assert c(ids=FAKE, top_k=0, E=4) == -5
+    h = lambda x=FAKE, dt=1, T=16, K=512, ids=None, top_k=0, E=1, chunk=1024, hess=FAKE: \
+        L.iq_hessian_collect(x, dt, T, K, ids, top_k, E, chunk, hess, None, None)
+    assert h(dt=5) == -2 and h(x=None) == -3 and h(hess=None) == -3
+    assert h(K=300) == -4 and h(T=-1) == -5 and h(E=2) == -5 and h(ids=FAKE, top_k=0, E=2) == -5
+    assert h(chunk=0) == -5 and h(ids=FAKE, top_k=2, E=1 << 22) == -5 and h(T=1 << 31) == -5
+    assert h(T=0) == 0                            # nothing to add: returns before any launch
     imp = lambda s=FAKE, cnt=FAKE, E=1, K=8, fl=1e-6, out=FAKE: L.iq_imatrix_importance(s, cnt, E, K, fl, out,
                                                                                        None, None)
     assert imp(s=None) == -3 and imp(out=None) == -3

@@ -325,6 +325,108 @@ def test_importance_parity(api, orc):
 
 
 # ---------------------------------------------------------------------------
+# Hessian diagonal blocks (the input to the local-Hessian choice search).
+# Small-integer activations make every product and partial sum exact in fp32,
+# so any summation order gives the oracle's value bit for bit; real-valued
+# activations are held to the recursive-summation bound n * u * sum|x_i x_j|
+# <= n * u * sqrt(H_ii H_jj) (Cauchy-Schwarz), n the expert's token count.
+# ---------------------------------------------------------------------------
+def _int_acts(T, K, seed):
+    return inputs.rng(seed).integers(-8, 9, size=(T, K)).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 37, 4096])
+def test_hessian_dense_exact(api, orc, dtype, T):
+    say("hessian dense exact", dtype, T)
+    K = 512  # 2 blocks: 20 tiles, so 4096 tokens run in 16 token ranges
+    x = _int_acts(T, K, 2500 + T)
+    got = host(api.hessian_collect(dev_w(x, dtype)))
+    want, st = orc.hessian_collect(x)
+    assert st == 0
+    assert np.array_equal(got, want.astype(np.float32))
+
+
+@pytest.mark.parametrize("chunk_rows", [1024, 100])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hessian_moe_exact(api, orc, chunk_rows, dtype):
+    say("hessian moe exact", chunk_rows, dtype)
+    T, K, E, top_k = 1500, 512, 6, 3
+    x = _int_acts(T, K, 2600)
+    ids = inputs.routing(T, top_k, E, 2601, n_idle=1)
+    ids[3] = [2, 2, 5]   # a duplicate id adds the token twice
+    ids[4] = [2, 2, 2]
+    st = api.new_status()
+    got = host(api.hessian_collect(dev_w(x, dtype), dev(ids), E, chunk_rows=chunk_rows, status=st))
+    want, st_o = orc.hessian_collect(x, ids, E)
+    assert int(host(st)[0]) == st_o == 0
+    assert np.array_equal(got, want.astype(np.float32))
+    _, counts, _ = orc.collect(x, ids, E)
+    assert np.all(got[counts == 0] == 0) and (counts == 0).sum() == 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hessian_real_values_within_bound(api, orc, dtype):
+    say("hessian real values", dtype)
+    T, K, E, top_k = 700, 768, 3, 2
+    x = inputs.activations(T, K, 2700, 2701, bf16=(dtype == "bf16"))
+    ids = inputs.routing(T, top_k, E, 2702, n_idle=0)
+    for rid in (None, ids):
+        E_ = 1 if rid is None else E
+        hd = api.hessian_collect(dev_w(x, dtype), None if rid is None else dev(rid), E_)
+        got = host(hd).copy()
+        want, _ = orc.hessian_collect(x, rid, E_)
+        n = np.full(E_, T) if rid is None else orc.collect(x, rid, E)[1]
+        d = np.einsum("ebii->ebi", want)
+        bound = n[:, None, None, None] * 2.0 ** -24 * np.sqrt(d[..., :, None] * d[..., None, :])
+        assert np.all(np.abs(got - want) <= bound)
+        assert np.array_equal(got, np.swapaxes(got, -1, -2))        # exactly symmetric
+        # accumulates in place: the second pass adds the same bits again
+        api.hessian_collect(dev_w(x, dtype), None if rid is None else dev(rid), E_, hess=hd)
+        assert np.array_equal(host(hd), 2 * got)
+
+
+def test_hessian_flags(api):
+    say("hessian flags")
+    x = np.ones((64, 256), np.float32)
+    x[10, 5] = np.inf
+    ids = np.zeros((64, 2), np.int32)
+    ids[:, 1] = 1
+    ids[20, 0] = 40      # out of range: skipped, flagged
+    st = api.new_status()
+    h = host(api.hessian_collect(dev(x), dev(ids), 4, status=st))
+    assert int(host(st)[0]) == 1 | 16
+    assert h[0, 0, 0, 0] == 63 and h[1, 0, 0, 0] == 64 and np.all(h[2:] == 0)
+
+
+def test_hessian_workload_sizes(api, orc):
+    """4096 bf16 tokens into 2048 columns (dense), and two experts of the
+    128-expert top-8 routing, against the oracle within the summation bound."""
+    say("hessian workload dense 4096x2048")
+    _, x, _, _ = inputs.workload("iq2_xs_5632x2048")
+    got = host(api.hessian_collect(dev_w(x, "bf16")))
+    want, _ = orc.hessian_collect(x)
+    d = np.einsum("ebii->ebi", want)
+    assert np.all(np.abs(got - want) <= x.shape[0] * 2.0 ** -24 * np.sqrt(d[..., :, None] * d[..., None, :]))
+    say("hessian workload moe 128 experts")
+    spec = inputs.MOE
+    E = spec["experts"]
+    xm = inputs.activations(spec["T"], spec["cols"], spec["x_sigma_seed"], spec["x_z_seed"], bf16=True)
+    ids = inputs.routing(spec["T"], spec["top_k"], E, spec["ids_seed"], spec["n_idle"])
+    got = host(api.hessian_collect(dev_w(xm, "bf16"), dev(ids), E))
+    _, counts, _ = orc.collect(xm, ids, E)
+    busy = int(np.argmax(counts))
+    pick = [busy, int(np.flatnonzero(counts > 0)[-1])]
+    sub = np.where(ids == pick[0], 0, np.where(ids == pick[1], 1, -1)).astype(np.int32)
+    want, _ = orc.hessian_collect(xm, sub, 2)
+    d = np.einsum("ebii->ebi", want)
+    n = counts[pick].astype(np.float64)
+    assert np.all(np.abs(got[pick] - want) <= n[:, None, None, None] * 2.0 ** -24 *
+                  np.sqrt(d[..., :, None] * d[..., None, :]))
+    assert np.all(got[counts == 0] == 0)
+
+
+# ---------------------------------------------------------------------------
 # The named workloads, end to end (GPU importance fed to both encoders)
 # ---------------------------------------------------------------------------
 def test_workload_iq2_xxs_256x512_end_to_end(api, orc):
