@@ -775,9 +775,11 @@ int orc_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, c
 /* rounded to fp32); R17 dw = w - w^ with w^ the decoder's values; the unit   */
 /* error is e = sum_i dw_i (sum_j H_ij dw_j), inner and outer sums fmaf       */
 /* chains in ascending index; R18 in the two passes unit u takes the first    */
-/* choice minimising f = fmaf(2, dw_u . r_u, e_u) where r_u,i = sum over the  */
-/* block's columns j outside u (ascending) of H_ij dw_j at the current picks; */
-/* a pick takes effect at once (units visited in ascending order).            */
+/* choice minimising f = fmaf(2, dw_u . r_u, e_u) where r_u = sum over the    */
+/* other units v of H_uv dw_v at the current picks, gathered unit by unit:    */
+/* each unit's contribution is an fmaf chain over its columns (ascending,     */
+/* from zero) and the contributions are added in ascending unit order; a pick */
+/* takes effect at once (units visited in ascending order).                   */
 /* ------------------------------------------------------------------------- */
 static float hd(const float *H, float lam, int i, int j) {
   float v = H[i * 256 + j];
@@ -834,9 +836,11 @@ static int choice_search_block(int fmt, const float *x, const float *a, const fl
       float r[32];
       for (int i = 0; i < UV; ++i) {
         float acc = 0.0f;
-        for (int j = 0; j < 256; ++j) {
-          if (j >= u * UV && j < (u + 1) * UV) continue;
-          acc = fmaf(hd(H, lam, u * UV + i, j), dwcur[j], acc);
+        for (int v = 0; v < U; ++v) {
+          if (v == u) continue;
+          float part = 0.0f;  /* H_uv dw_v, row i */
+          for (int j = v * UV; j < (v + 1) * UV; ++j) part = fmaf(hd(H, lam, u * UV + i, j), dwcur[j], part);
+          acc = acc + part;
         }
         r[i] = acc;
       }
