@@ -203,6 +203,41 @@ def main() -> int:
         extras["every_choice_5632x2048"] = ev
         log("every choice", ev)
 
+        # local-Hessian path: Hessian blocks from the same 4,096 tokens, the
+        # choice search (every-choice encode + unit picks + two passes), then
+        # the encode under the picked choices
+        def timed(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        hess = torch.zeros((1, cols // 256, 256, 256), dtype=torch.float32, device=dev)
+
+        def hess_fn():
+            hess.zero_()
+            api.hessian_collect(x, hess=hess)
+
+        lh = {"hessian_collect_ms": round(timed(hess_fn, args.reps), 4)}
+        hess_flops = 2.0 * T * cols * 256
+        lh["hessian_TFLOP_s"] = round(hess_flops / (lh["hessian_collect_ms"] * 1e-3) / 1e12, 2)
+        for f in api.FORMATS:
+            g = torch.from_numpy(inputs.grid_for(f, GRID_SEED[f])).to(dev)
+            chs = api.choice_search(f, w, g, hess, imp)
+            cs_ms = timed(lambda: api.choice_search(f, w, g, hess, imp, out=chs), max(2, args.reps // 3))
+            enc = time_encode(f, w, g, imp, choices=chs)
+            lh[f] = {"choice_search_ms": round(cs_ms, 4), "fixed_encode_ms": enc["encode_ms"],
+                     "path_ms": round(lh["hessian_collect_ms"] + cs_ms + enc["encode_ms"], 4)}
+            del chs
+        extras["local_hessian_5632x2048"] = lh
+        log("local hessian", lh)
+        del hess
+
         # IQ1 layouts on 17408x5120 (importance from 4,096 tokens)
         wl, xl, gl, sl = inputs.workload("iq1_s_17408x5120")
         wld, xld = to_dev_bf16(wl), to_dev_bf16(xl)

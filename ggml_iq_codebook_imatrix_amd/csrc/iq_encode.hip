@@ -712,12 +712,20 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
 // damped diagonal Hessian block, then revisit the units twice, each taking the
 // choice that most lowers the block error dw H dw^T with the others held.
 // Evaluation order (fp32, explicit fmaf): unit error e = sum_i dw_i (sum_j
-// H_ij dw_j), i and j ascending over the unit's columns; cross term r_i =
-// sum over the block's other columns j (ascending) of H_ij dw_j at the current
-// picks; a candidate scores fmaf(2, dw . r, e); first minimum wins.  The
-// damped block is H + lambda I, lambda = perc_damp * mean(diag H).
-// One wave per (expert, 64-row tile, block): lanes are rows, so every H_ij is
-// a wave-uniform scalar load shared by the 64 rows.
+// H_ij dw_j), i and j ascending over the unit's columns; the cross term
+// r = sum over the other units v of H_uv dw_v is gathered unit by unit (an
+// fmaf chain over v's columns from zero per unit, the units' parts added in
+// ascending order); a candidate scores fmaf(2, dw . r, e); first minimum wins.
+// The damped block is H + lambda I, lambda = perc_damp * mean(diag H).
+//
+// One workgroup per (expert, 64-row tile, block) with one wave per unit:
+// lanes are rows, so every H_ij is a wave-uniform scalar operand shared by the
+// 64 rows; wave v keeps its unit's current residual in registers.  Step A:
+// wave v scores every choice of unit v (the table of unit errors is kept in
+// LDS: a candidate's own-block error does not change between passes).  A
+// revisit of unit u: every other wave v forms its part H_uv dw_v, wave u adds
+// the parts in unit order, the waves score the choices of unit u between
+// them, and wave u takes the first minimum and decodes its new residual.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) damping_kernel(const float *__restrict__ hess, int64_t n, float perc_damp,
                                                        float *__restrict__ lam) {
@@ -746,87 +754,97 @@ __device__ __forceinline__ void unit_residual(const EncArgs &A, const uint8_t *e
 }
 
 template <int F>
-__global__ void __launch_bounds__(64) choice_search_kernel(EncArgs A, const uint8_t *__restrict__ every,
-                                                            int64_t stride, const float *__restrict__ hess,
-                                                            const float *__restrict__ lamv,
-                                                            uint8_t *__restrict__ choices) {
+__global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncArgs A, const uint8_t *__restrict__ every,
+                                                                          int64_t stride,
+                                                                          const float *__restrict__ hess,
+                                                                          const float *__restrict__ lamv,
+                                                                          uint8_t *__restrict__ choices) {
   using G = Geo<F>;
   constexpr int U = G::UNITS, UV = 8 * G::GPU, NC = G::NC;
-  __shared__ uint8_t s_pick[U][64];
+  __shared__ float s_q[U][NC][64];   // own-block error of every (unit, choice)
+  __shared__ float s_p[U][UV][64];   // parts H_uv dw_v of the unit being revisited
+  __shared__ float s_r[UV][64];      // its cross term
+  __shared__ float s_f[NC][64];      // its candidates' scores
   const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
   const int64_t tile = L % A.tiles_per_e;
   const int64_t q = L / A.tiles_per_e;
   const int b = static_cast<int>(q % A.nb);
   const int64_t e = q / A.nb;
-  const int lane = threadIdx.x;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's unit
+  const int lane = threadIdx.x & 63;
   const int64_t rin = tile * 64 + lane;
   const bool valid = rin < A.rpe;
   const int64_t r = e * A.rpe + (valid ? rin : A.rpe - 1);
   const float *H = hess + (e * A.nb + b) * 65536;
   const float lam = lamv[e * A.nb + b];
 
-  // each unit's best choice under its own damped block
-  for (int u = 0; u < U; ++u) {
+  // step A: every choice of unit v under its own damped block
+  float dwv[UV];
+  int pick = 0;
+  {
     float best = 0.0f;
-    int bc = 0;
     for (int c = 0; c < NC; ++c) {
       float dw[UV];
-      unit_residual<F>(A, every, stride, r, b, c, u, dw);
+      unit_residual<F>(A, every, stride, r, b, c, v, dw);
       float err = 0.0f;
 #pragma unroll
       for (int i = 0; i < UV; ++i) {
-        const float *Hi = H + (u * UV + i) * 256 + u * UV;
+        const float *Hi = H + (v * UV + i) * 256 + v * UV;
         float y = 0.0f;
 #pragma unroll
         for (int j = 0; j < UV; ++j) y = __builtin_fmaf(j == i ? Hi[j] + lam : Hi[j], dw[j], y);
         err = __builtin_fmaf(dw[i], y, err);
       }
-      if (c == 0 || err < best) { best = err; bc = c; }
+      s_q[v][c][lane] = err;
+      if (c == 0 || err < best) { best = err; pick = c; }
     }
-    s_pick[u][lane] = static_cast<uint8_t>(bc);
+    unit_residual<F>(A, every, stride, r, b, pick, v, dwv);
   }
-  // two passes: each unit takes the choice that most lowers the block error
+  // two passes over the units in ascending order
   for (int pass = 0; pass < 2; ++pass) {
     for (int u = 0; u < U; ++u) {
-      float rr[UV];
-#pragma unroll
-      for (int i = 0; i < UV; ++i) rr[i] = 0.0f;
-      for (int v = 0; v < U; ++v) {
-        if (v == u) continue;
-        float dv[UV];
-        unit_residual<F>(A, every, stride, r, b, s_pick[v][lane], v, dv);
+      if (v != u) {
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
           const float *Hi = H + (u * UV + i) * 256 + v * UV;
+          float part = 0.0f;
 #pragma unroll
-          for (int j = 0; j < UV; ++j) rr[i] = __builtin_fmaf(Hi[j], dv[j], rr[i]);
+          for (int j = 0; j < UV; ++j) part = __builtin_fmaf(Hi[j], dwv[j], part);
+          s_p[v][i][lane] = part;
         }
       }
-      float best = 0.0f;
-      int bc = 0;
-      for (int c = 0; c < NC; ++c) {
-        float dw[UV];
-        unit_residual<F>(A, every, stride, r, b, c, u, dw);
-        float err = 0.0f, dot = 0.0f;
+      __syncthreads();
+      if (v == u) {
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
-          const float *Hi = H + (u * UV + i) * 256 + u * UV;
-          float y = 0.0f;
-#pragma unroll
-          for (int j = 0; j < UV; ++j) y = __builtin_fmaf(j == i ? Hi[j] + lam : Hi[j], dw[j], y);
-          err = __builtin_fmaf(dw[i], y, err);
+          float acc = 0.0f;
+          for (int w = 0; w < U; ++w)
+            if (w != u) acc = acc + s_p[w][i][lane];
+          s_r[i][lane] = acc;
         }
-#pragma unroll
-        for (int i = 0; i < UV; ++i) dot = __builtin_fmaf(dw[i], rr[i], dot);
-        const float f = __builtin_fmaf(2.0f, dot, err);
-        if (c == 0 || f < best) { best = f; bc = c; }
       }
-      s_pick[u][lane] = static_cast<uint8_t>(bc);
+      __syncthreads();
+      for (int c = v; c < NC; c += U) {
+        float dw[UV];
+        unit_residual<F>(A, every, stride, r, b, c, u, dw);
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UV; ++i) dot = __builtin_fmaf(dw[i], s_r[i][lane], dot);
+        s_f[c][lane] = __builtin_fmaf(2.0f, dot, s_q[u][c][lane]);
+      }
+      __syncthreads();
+      if (v == u) {
+        float best = s_f[0][lane];
+        pick = 0;
+        for (int c = 1; c < NC; ++c) {
+          const float f = s_f[c][lane];
+          if (f < best) { best = f; pick = c; }
+        }
+        unit_residual<F>(A, every, stride, r, b, pick, v, dwv);
+      }
     }
   }
-  if (!valid) return;
-#pragma unroll
-  for (int u = 0; u < U; ++u) choices[(r * A.nb + b) * U + u] = s_pick[u][lane];
+  if (valid) choices[(r * A.nb + b) * U + v] = static_cast<uint8_t>(pick);
 }
 
 // ---------------------------------------------------------------------------
@@ -937,7 +955,8 @@ static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp,
                      perc_damp, lam);
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb;
-  hipLaunchKernelGGL(choice_search_kernel<F>, dim3(static_cast<unsigned>(A.total_wg)), dim3(64), 0, stream, A,
+  hipLaunchKernelGGL(choice_search_kernel<F>, dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::UNITS), 0,
+                     stream, A,
                      static_cast<const uint8_t *>(every), E.copy_stride, hess, static_cast<const float *>(lam),
                      choices);
   const hipError_t le = hipGetLastError();
