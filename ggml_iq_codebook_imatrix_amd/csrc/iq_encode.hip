@@ -307,6 +307,17 @@ __device__ __forceinline__ void rescan_chunk(const float *__restrict__ grid, con
   }
 }
 
+// One group's fields in a packed block: grid index k, sign mask (IQ2), local
+// scale ls, delta sign h (IQ1), and the block's fp16 scale bits d16.
+struct GroupFields {
+  uint32_t d16, k, mask, ls, h;
+};
+
+// A group's fields as one word: k | mask << 11 | ls << 19 | h << 23.
+__device__ __forceinline__ uint32_t pack_record(const GroupFields &f) {
+  return f.k | (f.mask << 11) | (f.ls << 19) | (f.h << 23);
+}
+
 // ---------------------------------------------------------------------------
 // Pack one workgroup's bytes of one row's block from the LDS field tables:
 // k[g][row], m[g][row] (IQ2 sign mask / IQ1 shift), c[u][row] (unit choice).
@@ -372,8 +383,9 @@ __device__ __forceinline__ void pack_bytes(uint8_t *blk, int sb, int lane, const
 // ---------------------------------------------------------------------------
 // MODE: SEARCH scores every choice per unit; FIXED takes the caller's choices;
 // EVERY writes one payload per choice (out[c] == the FIXED payload with every
-// unit set to c) from a single sweep.
-enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2 };
+// unit set to c) from a single sweep; RECORDS writes the same groups' fields
+// as one word per (choice, group, row) for the choice search.
+enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2, RECORDS = 3 };
 
 template <int F, int MODE>
 __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
@@ -511,6 +523,32 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
     }
   }
 
+  // ---- every choice: one field record per choice and group ----------------
+  if (MODE == RECORDS) {
+    uint32_t *rp = A.rec + (static_cast<int64_t>(b) * 32 + gi) * A.rows + r;
+    const int64_t cstride = static_cast<int64_t>(A.nb) * 32 * A.rows;
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+      int slot = c;
+      if (F == IQ1_M) slot = (best[8 + c] < best[c]) ? 8 + c : c;  // tie: the lower shift
+      int chs = bidx[c];
+      if (F == IQ1_M) chs = (slot != c) ? bidx[8 + c] : chs;
+      const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
+      int kb;
+      uint32_t mfield;
+      rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      GroupFields f;
+      f.d16 = d16;
+      f.k = static_cast<uint32_t>(kb);
+      f.mask = G::IQ1 ? 0u : mfield;
+      f.ls = static_cast<uint32_t>(F == IQ1_S ? (c & 7) : c);
+      f.h = F == IQ1_S ? static_cast<uint32_t>(c >> 3) : (F == IQ1_M ? mfield : 0u);
+      if (d16 == 0) { f.k = 0; f.mask = 0; f.ls = 0; f.h = 0; }
+      if (valid) rp[c * cstride] = pack_record(f);
+    }
+    return;
+  }
+
   // ---- every choice: one payload per choice --------------------------------
   if (MODE == EVERY) {
 #pragma unroll
@@ -624,49 +662,58 @@ __device__ __forceinline__ uint32_t ld16(const uint8_t *p) { return *reinterpret
 
 // Decode group g (0..31) of one block into 8 fp32 values.
 template <int F>
-__device__ __forceinline__ void decode_group(const uint8_t *blk, int g, const float *__restrict__ grid, float y[8]) {
+__device__ __forceinline__ GroupFields group_fields(const uint8_t *blk, int g) {
   using G = Geo<F>;
-  uint32_t d16, k, mask = 0, h = 0, ls;
+  GroupFields f;
+  f.mask = 0;
+  f.h = 0;
   const int u = g / G::GPU;
   if (F == IQ2_XXS) {
-    d16 = ld16(blk);
+    f.d16 = ld16(blk);
     const int ib = g >> 2, l = g & 3;
     const uint32_t word = ld16(blk + 2 + 8 * ib + 4) | (ld16(blk + 2 + 8 * ib + 6) << 16);
-    k = blk[2 + 8 * ib + l];
+    f.k = blk[2 + 8 * ib + l];
     const uint32_t si = (word >> (7 * l)) & 0x7fu;
-    mask = si | ((__builtin_popcount(si) & 1u) << 7);
-    ls = word >> 28;
+    f.mask = si | ((__builtin_popcount(si) & 1u) << 7);
+    f.ls = word >> 28;
   } else if (F == IQ2_XS) {
-    d16 = ld16(blk);
+    f.d16 = ld16(blk);
     const uint32_t v = ld16(blk + 2 + 2 * g);
-    k = v & 511u;
+    f.k = v & 511u;
     const uint32_t si = v >> 9;
-    mask = si | ((__builtin_popcount(si) & 1u) << 7);
+    f.mask = si | ((__builtin_popcount(si) & 1u) << 7);
     const uint32_t sbyte = blk[66 + (u >> 1)];
-    ls = (u & 1) ? (sbyte >> 4) : (sbyte & 15u);
+    f.ls = (u & 1) ? (sbyte >> 4) : (sbyte & 15u);
   } else if (F == IQ2_S) {
-    d16 = ld16(blk);
-    k = blk[2 + g] | (((blk[66 + (g >> 2)] >> (2 * (g & 3))) & 3u) << 8);
-    mask = blk[34 + g];
+    f.d16 = ld16(blk);
+    f.k = blk[2 + g] | (((blk[66 + (g >> 2)] >> (2 * (g & 3))) & 3u) << 8);
+    f.mask = blk[34 + g];
     const uint32_t sbyte = blk[74 + (u >> 1)];
-    ls = (u & 1) ? (sbyte >> 4) : (sbyte & 15u);
+    f.ls = (u & 1) ? (sbyte >> 4) : (sbyte & 15u);
   } else if (F == IQ1_S) {
-    d16 = ld16(blk);
+    f.d16 = ld16(blk);
     const uint32_t w = ld16(blk + 34 + 2 * (g >> 2));
-    k = blk[2 + g] | (((w >> (3 * (g & 3))) & 7u) << 8);
-    ls = (w >> 12) & 7u;
-    h = w >> 15;
+    f.k = blk[2 + g] | (((w >> (3 * (g & 3))) & 7u) << 8);
+    f.ls = (w >> 12) & 7u;
+    f.h = w >> 15;
   } else {
-    d16 = 0;
+    f.d16 = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) d16 |= (ld16(blk + 48 + 2 * w) >> 12) << (4 * w);
+    for (int w = 0; w < 4; ++w) f.d16 |= (ld16(blk + 48 + 2 * w) >> 12) << (4 * w);
     const uint32_t nb = blk[32 + (g >> 1)];
     const uint32_t nib = (g & 1) ? (nb >> 4) : (nb & 15u);
-    k = blk[g] | ((nib & 7u) << 8);
-    h = nib >> 3;
-    ls = (ld16(blk + 48 + 2 * (u >> 2)) >> (3 * (u & 3))) & 7u;
+    f.k = blk[g] | ((nib & 7u) << 8);
+    f.h = nib >> 3;
+    f.ls = (ld16(blk + 48 + 2 * (u >> 2)) >> (3 * (u & 3))) & 7u;
   }
-  const float d = f16_bits_to_f32(static_cast<uint16_t>(d16));
+  return f;
+}
+
+// The group's 8 values from its fields (d: the block scale as fp32).
+template <int F>
+__device__ __forceinline__ void group_values(float d, uint32_t k, uint32_t mask, uint32_t ls, uint32_t h,
+                                             const float *__restrict__ grid, float y[8]) {
+  using G = Geo<F>;
   float gv[8];
   load_entry(grid + static_cast<int64_t>(k) * 8, gv);
   if (!G::IQ1) {
@@ -682,6 +729,12 @@ __device__ __forceinline__ void decode_group(const uint8_t *blk, int g, const fl
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = s * (gv[j] + delta);
   }
+}
+
+template <int F>
+__device__ __forceinline__ void decode_group(const uint8_t *blk, int g, const float *__restrict__ grid, float y[8]) {
+  const GroupFields f = group_fields<F>(blk, g);
+  group_values<F>(f16_bits_to_f32(static_cast<uint16_t>(f.d16)), f.k, f.mask, f.ls, f.h, grid, y);
 }
 
 template <int F>
@@ -707,6 +760,34 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Local-Hessian choice search (ModelOpt PR #3158).  Damping of the diagonal
+// Hessian blocks: lambda = perc_damp * mean(diag H_b), the diagonal summed in
+// fp64 and the mean rounded to fp32.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) damping_kernel(const float *__restrict__ hess, int64_t n, float perc_damp,
+                                                       float *__restrict__ lam) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float *H = hess + i * 65536;
+  double acc = 0.0;
+  for (int j = 0; j < 256; ++j) acc += static_cast<double>(H[j * 257]);
+  lam[i] = perc_damp * static_cast<float>(acc / 256.0);
+}
+
+// the unit's weights (the same under every choice)
+template <int F>
+__device__ __forceinline__ void unit_weights(const EncArgs &A, int64_t r, int b, int u, float *x) {
+  using G = Geo<F>;
+#pragma unroll
+  for (int gi = 0; gi < G::GPU; ++gi)
+    load8(A.w, A.dtype, r * A.cols + static_cast<int64_t>(b) * 256 + (u * G::GPU + gi) * 8, x + gi * 8);
+}
+
+template <int F>
+__device__ __forceinline__ void record_values(float d, uint32_t rec, const float *__restrict__ grid, float y[8]) {
+  group_values<F>(d, rec & 2047u, (rec >> 11) & 255u, (rec >> 19) & 15u, (rec >> 23) & 1u, grid, y);
+}
+
 // Local-Hessian choice search (ModelOpt PR #3158's choice_search): from the
 // payloads of every choice, give each unit its best choice under its own
 // damped diagonal Hessian block, then revisit the units twice, each taking the
@@ -719,51 +800,33 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
 // The damped block is H + lambda I, lambda = perc_damp * mean(diag H).
 //
 // One workgroup per (expert, 64-row tile, block) with one wave per unit:
-// lanes are rows, so every H_ij is a wave-uniform scalar operand shared by the
-// 64 rows; wave v keeps its unit's current residual in registers.  Step A:
-// wave v scores every choice of unit v (the table of unit errors is kept in
-// LDS: a candidate's own-block error does not change between passes).  A
-// revisit of unit u: every other wave v forms its part H_uv dw_v, wave u adds
-// the parts in unit order, the waves score the choices of unit u between
-// them, and wave u takes the first minimum and decodes its new residual.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) damping_kernel(const float *__restrict__ hess, int64_t n, float perc_damp,
-                                                       float *__restrict__ lam) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const float *H = hess + i * 65536;
-  double acc = 0.0;
-  for (int j = 0; j < 256; ++j) acc += static_cast<double>(H[j * 257]);
-  lam[i] = perc_damp * static_cast<float>(acc / 256.0);
-}
-
+// lanes are rows, so every H_ij is a wave-uniform operand shared by the 64
+// rows; wave v keeps its unit's weights and current residual in registers.
+// The every-choice sweep hands over each group's fields under every choice as
+// one word per (choice, group, row), rows contiguous, so the residuals come
+// from coalesced loads rather than from packed bytes.  Step A: wave v scores
+// every choice of unit v; the own-block errors do not change between passes,
+// so each wave keeps those of the choices it scores later.  A revisit of unit u: every
+// other wave v forms its part H_uv dw_v; the waves add the parts in unit order
+// (each a slice of the rows of r); the waves score unit u's choices between
+// them, with u's weights passed through LDS; wave u takes the first minimum.
 template <int F>
-__device__ __forceinline__ void unit_residual(const EncArgs &A, const uint8_t *every, int64_t stride, int64_t r,
-                                              int b, int c, int u, float *dw) {
-  using G = Geo<F>;
-  const uint8_t *blk = every + c * stride + (r * A.nb + b) * G::BYTES;
-#pragma unroll
-  for (int gi = 0; gi < G::GPU; ++gi) {
-    const int g = u * G::GPU + gi;
-    float y[8], x[8];
-    decode_group<F>(blk, g, A.grid, y);
-    load8(A.w, A.dtype, r * A.cols + static_cast<int64_t>(b) * 256 + g * 8, x);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dw[gi * 8 + j] = x[j] - y[j];
-  }
-}
-
-template <int F>
-__global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncArgs A, const uint8_t *__restrict__ every,
-                                                                          int64_t stride,
+__global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncArgs A, const uint32_t *__restrict__ rec,
+                                                                          const uint16_t *__restrict__ dblk,
                                                                           const float *__restrict__ hess,
                                                                           const float *__restrict__ lamv,
                                                                           uint8_t *__restrict__ choices) {
   using G = Geo<F>;
-  constexpr int U = G::UNITS, UV = 8 * G::GPU, NC = G::NC;
-  __shared__ float s_q[U][NC][64];   // own-block error of every (unit, choice)
-  __shared__ float s_p[U][UV][64];   // parts H_uv dw_v of the unit being revisited
+  constexpr int U = G::UNITS, UV = 8 * G::GPU, NC = G::NC, GPU = G::GPU;
+  constexpr int CB = F == IQ1_M ? 2 : 4;    // choices scored together in step A (one pass over H_vv)
+  constexpr int NCW = (NC + U - 1) / U;     // choices of the revisited unit scored per wave
+  constexpr int NI = (UV + U - 1) / U;      // cross-term rows summed per wave
+  static_assert(NC % CB == 0 && U * NC <= U * UV, "choice batches; the error table fits the parts buffer");
+  // s_buf holds the table of own-block errors [unit][choice][row] after step A,
+  // then the parts H_uv dw_v [v][i][row] of the unit being revisited
+  __shared__ float s_buf[U * UV * 64];
   __shared__ float s_r[UV][64];      // its cross term
+  __shared__ float s_x[UV][64];      // its weights
   __shared__ float s_f[NC][64];      // its candidates' scores
   const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
   const int64_t tile = L % A.tiles_per_e;
@@ -777,32 +840,88 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   const int64_t r = e * A.rpe + (valid ? rin : A.rpe - 1);
   const float *H = hess + (e * A.nb + b) * 65536;
   const float lam = lamv[e * A.nb + b];
+  // record of (choice c, group g) for this lane's row
+  const int64_t rstride = A.rows;
+  const uint32_t *rrow = rec + static_cast<int64_t>(b) * 32 * rstride + r;
+  const int64_t cstride = A.nb * 32 * rstride;
 
-  // step A: every choice of unit v under its own damped block
-  float dwv[UV];
+  // step A: every choice of unit v under its own damped block, CB at a time
+  float xv[UV], dwv[UV];
+  unit_weights<F>(A, r, b, v, xv);
+  const float d = f16_bits_to_f32(dblk[r * A.nb + b]);
   int pick = 0;
   {
     float best = 0.0f;
-    for (int c = 0; c < NC; ++c) {
-      float dw[UV];
-      unit_residual<F>(A, every, stride, r, b, c, v, dw);
-      float err = 0.0f;
+#pragma unroll 1
+    for (int c0 = 0; c0 < NC; c0 += CB) {
+      float dw[CB][UV];
+#pragma unroll
+      for (int k = 0; k < CB; ++k) {
+#pragma unroll
+        for (int gi = 0; gi < GPU; ++gi) {
+          float y[8];
+          record_values<F>(d, rrow[(c0 + k) * cstride + (v * GPU + gi) * rstride], A.grid, y);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dw[k][gi * 8 + j] = xv[gi * 8 + j] - y[j];
+        }
+      }
+      // H_vv is streamed on every batch: kept live across batches it would
+      // not fit the scalar registers
+      const float *Hv = H;
+      asm volatile("" : "+s"(Hv));
+      float err[CB];
+#pragma unroll
+      for (int k = 0; k < CB; ++k) err[k] = 0.0f;
 #pragma unroll
       for (int i = 0; i < UV; ++i) {
-        const float *Hi = H + (v * UV + i) * 256 + v * UV;
-        float y = 0.0f;
+        const float *Hi = Hv + (v * UV + i) * 256 + v * UV;
+        float y[CB];
 #pragma unroll
-        for (int j = 0; j < UV; ++j) y = __builtin_fmaf(j == i ? Hi[j] + lam : Hi[j], dw[j], y);
-        err = __builtin_fmaf(dw[i], y, err);
+        for (int k = 0; k < CB; ++k) y[k] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < UV; ++j) {
+          const float h = j == i ? Hi[j] + lam : Hi[j];
+#pragma unroll
+          for (int k = 0; k < CB; ++k) y[k] = __builtin_fmaf(h, dw[k][j], y[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < CB; ++k) err[k] = __builtin_fmaf(dw[k][i], y[k], err[k]);
       }
-      s_q[v][c][lane] = err;
-      if (c == 0 || err < best) { best = err; pick = c; }
+#pragma unroll
+      for (int k = 0; k < CB; ++k) {
+        s_buf[(v * NC + c0 + k) * 64 + lane] = err[k];
+        if (c0 + k == 0 || err[k] < best) { best = err[k]; pick = c0 + k; }
+      }
     }
-    unit_residual<F>(A, every, stride, r, b, pick, v, dwv);
   }
+#pragma unroll
+  for (int gi = 0; gi < GPU; ++gi) {
+    float y[8];
+    record_values<F>(d, rrow[pick * cstride + (v * GPU + gi) * rstride], A.grid, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dwv[gi * 8 + j] = xv[gi * 8 + j] - y[j];
+  }
+  __syncthreads();
+  // each wave keeps the errors of the choices it scores in the passes
+  float qk[NCW][U];
+#pragma unroll
+  for (int k = 0; k < NCW; ++k)
+#pragma unroll
+    for (int u = 0; u < U; ++u) qk[k][u] = v + U * k < NC ? s_buf[(u * NC + v + U * k) * 64 + lane] : 0.0f;
+  __syncthreads();
   // two passes over the units in ascending order
+#pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll 1
     for (int u = 0; u < U; ++u) {
+      // the fields of this wave's share of unit u's choices do not depend on
+      // the picks: their loads are issued before the parts are formed
+      uint32_t rc[NCW][GPU];
+#pragma unroll
+      for (int k = 0; k < NCW; ++k)
+#pragma unroll
+        for (int gi = 0; gi < GPU; ++gi)
+          rc[k][gi] = v + U * k < NC ? rrow[(v + U * k) * cstride + (u * GPU + gi) * rstride] : 0u;
       if (v != u) {
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
@@ -810,27 +929,43 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
           float part = 0.0f;
 #pragma unroll
           for (int j = 0; j < UV; ++j) part = __builtin_fmaf(Hi[j], dwv[j], part);
-          s_p[v][i][lane] = part;
+          s_buf[(v * UV + i) * 64 + lane] = part;
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < UV; ++i) s_x[i][lane] = xv[i];
       }
       __syncthreads();
-      if (v == u) {
+      // cross term rows i = v, v + U, ...: the parts added in unit order
 #pragma unroll
-        for (int i = 0; i < UV; ++i) {
+      for (int t = 0; t < NI; ++t) {
+        const int i = v + U * t;
+        if (i < UV) {
           float acc = 0.0f;
           for (int w = 0; w < U; ++w)
-            if (w != u) acc = acc + s_p[w][i][lane];
+            if (w != u) acc = acc + s_buf[(w * UV + i) * 64 + lane];
           s_r[i][lane] = acc;
         }
       }
       __syncthreads();
-      for (int c = v; c < NC; c += U) {
-        float dw[UV];
-        unit_residual<F>(A, every, stride, r, b, c, u, dw);
-        float dot = 0.0f;
 #pragma unroll
-        for (int i = 0; i < UV; ++i) dot = __builtin_fmaf(dw[i], s_r[i][lane], dot);
-        s_f[c][lane] = __builtin_fmaf(2.0f, dot, s_q[u][c][lane]);
+      for (int k = 0; k < NCW; ++k) {
+        const int c = v + U * k;
+        if (c < NC) {
+          float qu = qk[k][0];
+#pragma unroll
+          for (int w = 1; w < U; ++w) qu = u == w ? qk[k][w] : qu;
+          float dot = 0.0f;
+#pragma unroll
+          for (int gi = 0; gi < GPU; ++gi) {
+            float y[8];
+            record_values<F>(d, rc[k][gi], A.grid, y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              dot = __builtin_fmaf(s_x[gi * 8 + j][lane] - y[j], s_r[gi * 8 + j][lane], dot);
+          }
+          s_f[c][lane] = __builtin_fmaf(2.0f, dot, qu);
+        }
       }
       __syncthreads();
       if (v == u) {
@@ -840,7 +975,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
           const float f = s_f[c][lane];
           if (f < best) { best = f; pick = c; }
         }
-        unit_residual<F>(A, every, stride, r, b, pick, v, dwv);
+#pragma unroll
+        for (int gi = 0; gi < GPU; ++gi) {
+          float y[8];
+          record_values<F>(d, rrow[pick * cstride + (v * GPU + gi) * rstride], A.grid, y);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dwv[gi * 8 + j] = xv[gi * 8 + j] - y[j];
+        }
       }
     }
   }
@@ -851,7 +992,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
 // Host launchers
 // ---------------------------------------------------------------------------
 template <int F>
-static int launch_quantize_t(EncArgs A, bool every, hipStream_t stream) {
+static int launch_quantize_t(EncArgs A, int mode, hipStream_t stream) {
   using G = Geo<F>;
   const int64_t nblocks = A.rows * A.nb;
   if (nblocks == 0) return 0;
@@ -887,25 +1028,29 @@ static int launch_quantize_t(EncArgs A, bool every, hipStream_t stream) {
   take_search_events(&ev0, &ev1);
   if (ev0) hipEventRecord(ev0, stream);
   const dim3 grid_dim(static_cast<unsigned>(A.total_wg)), block_dim(64 * G::WGG);
-  if (every)
+  if (mode == RECORDS)
+    hipLaunchKernelGGL((search_kernel<F, RECORDS>), grid_dim, block_dim, 0, stream, A);
+  else if (mode == EVERY)
     hipLaunchKernelGGL((search_kernel<F, EVERY>), grid_dim, block_dim, 0, stream, A);
   else if (A.choices)
     hipLaunchKernelGGL((search_kernel<F, FIXED_CHOICES>), grid_dim, block_dim, 0, stream, A);
   else
     hipLaunchKernelGGL((search_kernel<F, SEARCH>), grid_dim, block_dim, 0, stream, A);
-  const hipError_t le = hipGetLastError();
+  hipError_t le = hipGetLastError();
   if (ev1) hipEventRecord(ev1, stream);
+  if (le == hipSuccess && A.d_out)
+    le = hipMemcpyAsync(A.d_out, A.dscr, dbytes, hipMemcpyDeviceToDevice, stream);
   hipFreeAsync(scratch, stream);
   return le == hipSuccess ? 0 : -1;
 }
 
 int launch_quantize(int fmt, EncArgs A, bool every, hipStream_t stream) {
   switch (fmt) {
-    case IQ2_XXS: return launch_quantize_t<IQ2_XXS>(A, every, stream);
-    case IQ2_XS: return launch_quantize_t<IQ2_XS>(A, every, stream);
-    case IQ2_S: return launch_quantize_t<IQ2_S>(A, every, stream);
-    case IQ1_S: return launch_quantize_t<IQ1_S>(A, every, stream);
-    case IQ1_M: return launch_quantize_t<IQ1_M>(A, every, stream);
+    case IQ2_XXS: return launch_quantize_t<IQ2_XXS>(A, every ? EVERY : SEARCH, stream);
+    case IQ2_XS: return launch_quantize_t<IQ2_XS>(A, every ? EVERY : SEARCH, stream);
+    case IQ2_S: return launch_quantize_t<IQ2_S>(A, every ? EVERY : SEARCH, stream);
+    case IQ1_S: return launch_quantize_t<IQ1_S>(A, every ? EVERY : SEARCH, stream);
+    case IQ1_M: return launch_quantize_t<IQ1_M>(A, every ? EVERY : SEARCH, stream);
   }
   return -1;
 }
@@ -938,27 +1083,27 @@ static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp,
   using G = Geo<F>;
   const int64_t nblocks = A.rows * A.nb;
   if (nblocks == 0) return 0;
-  const size_t pbytes = static_cast<size_t>(G::NC) * nblocks * G::BYTES;
   const int64_t nl = A.E * A.nb;
+  const size_t rbytes = static_cast<size_t>(G::NC) * nblocks * 32 * sizeof(uint32_t);
+  const size_t doff = (rbytes + 255) & ~size_t(255);
+  const size_t loff = doff + ((nblocks * sizeof(uint16_t) + 255) & ~size_t(255));
   void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, ((pbytes + 255) & ~size_t(255)) + nl * sizeof(float), stream) != hipSuccess)
-    return -1;
-  uint8_t *every = static_cast<uint8_t *>(scratch);
-  float *lam = reinterpret_cast<float *>(static_cast<char *>(scratch) + ((pbytes + 255) & ~size_t(255)));
+  if (hipMallocAsync(&scratch, loff + nl * sizeof(float), stream) != hipSuccess) return -1;
+  uint32_t *rec = static_cast<uint32_t *>(scratch);
+  uint16_t *dblk = reinterpret_cast<uint16_t *>(static_cast<char *>(scratch) + doff);
+  float *lam = reinterpret_cast<float *>(static_cast<char *>(scratch) + loff);
   EncArgs E = A;
-  E.out = every;
   E.choices = nullptr;
-  E.copies = G::NC;
-  E.copy_stride = nblocks * G::BYTES;
-  int rc = launch_quantize_t<F>(E, true, stream);
+  E.rec = rec;
+  E.d_out = dblk;
+  int rc = launch_quantize_t<F>(E, RECORDS, stream);
   hipLaunchKernelGGL(damping_kernel, dim3(static_cast<unsigned>((nl + 255) / 256)), dim3(256), 0, stream, hess, nl,
                      perc_damp, lam);
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb;
   hipLaunchKernelGGL(choice_search_kernel<F>, dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::UNITS), 0,
-                     stream, A,
-                     static_cast<const uint8_t *>(every), E.copy_stride, hess, static_cast<const float *>(lam),
-                     choices);
+                     stream, A, static_cast<const uint32_t *>(rec), static_cast<const uint16_t *>(dblk), hess,
+                     static_cast<const float *>(lam), choices);
   const hipError_t le = hipGetLastError();
   hipFreeAsync(scratch, stream);
   return (rc == 0 && le == hipSuccess) ? 0 : -1;

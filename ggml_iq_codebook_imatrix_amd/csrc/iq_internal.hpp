@@ -18,6 +18,8 @@ struct EncArgs {
   uint8_t *out;
   int64_t copies, copy_stride;  // payload copies (every-choice: num_choices) and bytes between them
   int32_t *status;
+  uint32_t *rec;           // field records (choice search): [num_choices][nb][32 groups][rows]
+  uint16_t *d_out;         // copy of the fp16 block scales [rows][nb] (choice search), or null
   // filled by the launcher
   float *gtab;             // weighted norms [tables][NG][N]
   int64_t gtab_e_stride, gtab_cg_stride;
