@@ -307,6 +307,38 @@ __device__ __forceinline__ void rescan_chunk(const float *__restrict__ grid, con
   }
 }
 
+// IQ2 layouts rescan from a copy of the grid in LDS: chunk c's entry i sits at
+// float (32 c + i) * 8 + 4 c, so lanes rescanning different chunks read
+// different banks.  The weighted norm G_k is recomputed in the lane with the
+// same fmaf chain that built the table the sweep read, so it is the same value.
+__device__ __forceinline__ int lds_entry(int k) { return k * 8 + (k >> 5) * 4; }
+
+template <int F>
+__device__ __forceinline__ void rescan_chunk_lds(const float *s_grid, const float a[8], const GroupState<F> &S,
+                                                 int chs, float ssel, int &kb, uint32_t &mfield) {
+  constexpr int CH = 32;
+  float bt = __builtin_inff();
+  kb = chs * CH;
+  const float *base = s_grid + lds_entry(chs * CH);
+#pragma unroll 4
+  for (int i = 0; i < CH; ++i) {
+    float g[8];
+    load_entry(base + i * 8, g);
+    float gk = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gk = __builtin_fmaf(a[j], g[j] * g[j], gk);
+    const float t = __builtin_fmaf(ssel, gk, S.term(g));
+    if (t < bt) { bt = t; kb = chs * CH + i; }
+  }
+  uint32_t mask = S.neg;
+  if (S.odd) {
+    float g[8];
+    load_entry(s_grid + lds_entry(kb), g);
+    mask ^= 1u << S.flip_index(g);
+  }
+  mfield = mask;
+}
+
 // One group's fields in a packed block: grid index k, sign mask (IQ2), local
 // scale ls, delta sign h (IQ1), and the block's fp16 scale bits d16.
 struct GroupFields {
@@ -378,6 +410,16 @@ __device__ __forceinline__ void pack_bytes(uint8_t *blk, int sb, int lane, const
   }
 }
 
+// Copy the grid into LDS in the rescan layout (whole workgroup; ends with a barrier).
+template <int N>
+__device__ __forceinline__ void stage_grid(const float *__restrict__ grid, float *s_grid) {
+  for (int i = threadIdx.x; i < N * 2; i += blockDim.x) {
+    const int k = i >> 1;
+    *reinterpret_cast<float4 *>(s_grid + lds_entry(k) + (i & 1) * 4) = reinterpret_cast<const float4 *>(grid)[i];
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Search + pack.  Workgroup = WGG waves (groups) x 64 rows of one expert.
 // ---------------------------------------------------------------------------
@@ -388,7 +430,7 @@ __device__ __forceinline__ void pack_bytes(uint8_t *blk, int sb, int lane, const
 enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2, RECORDS = 3 };
 
 template <int F, int MODE>
-__global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
+__global__ void __launch_bounds__(64 * Geo<F>::WGG, 4) search_kernel(EncArgs A) {
   using G = Geo<F>;
   constexpr bool FIXED = MODE == FIXED_CHOICES;
   constexpr int WGG = G::WGG, GPU = G::GPU, N = G::N;
@@ -399,7 +441,12 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   // fixed choices: one slot (IQ1_M: its two shifts)
   constexpr int NSLOT = FIXED ? (F == IQ1_M ? 2 : 1) : 16;
 
-  __shared__ float s_best[MODE == SEARCH ? WGG : 1][MODE == SEARCH ? NSLOT : 1][64];
+  // s_u: the per-slot minima exchanged for scoring (search), then, for the IQ2
+  // layouts, the grid copy the rescans read
+  constexpr int BEST_F = MODE == SEARCH ? WGG * NSLOT * 64 : 1;
+  constexpr int GRID_F = G::IQ1 ? 1 : N * 8 + (N / 32) * 4;
+  __shared__ __attribute__((aligned(16))) float s_u[BEST_F > GRID_F ? BEST_F : GRID_F];
+  float (*s_best)[NSLOT][64] = reinterpret_cast<float (*)[NSLOT][64]>(s_u);
   __shared__ uint16_t s_k[WGG][64];
   __shared__ uint8_t s_m[WGG][64];
   __shared__ uint8_t s_c[UPW][64];
@@ -524,6 +571,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   }
 
   // ---- every choice: one field record per choice and group ----------------
+  if (!G::IQ1 && MODE != SEARCH) stage_grid<N>(A.grid, s_u);
   if (MODE == RECORDS) {
     uint32_t *rp = A.rec + (static_cast<int64_t>(b) * 32 + gi) * A.rows + r;
     const int64_t cstride = static_cast<int64_t>(A.nb) * 32 * A.rows;
@@ -536,7 +584,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      if (G::IQ1) rescan_chunk<F>(A.grid, gt, S, chs, ssel, slot >> 3, kb, mfield);
+      else rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
       GroupFields f;
       f.d16 = d16;
       f.k = static_cast<uint32_t>(kb);
@@ -560,7 +609,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      if (G::IQ1) rescan_chunk<F>(A.grid, gt, S, chs, ssel, slot >> 3, kb, mfield);
+      else rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
       int cu = c;
       if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
       __syncthreads();  // the previous choice's bytes have been read from LDS
@@ -643,7 +693,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   }
   int kb;
   uint32_t mfield;
-  rescan_chunk<F>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
+  if (G::IQ1) {
+    rescan_chunk<F>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
+  } else {
+    if (MODE == SEARCH) __syncthreads();  // every wave has read the minima
+    stage_grid<N>(A.grid, s_u);
+    rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
+  }
   if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
 
   // ---- pack ----------------------------------------------------------------
