@@ -14,11 +14,13 @@
 //
 // Design.  No floating-point atomics: a pass marks, per 1,024-row chunk and
 // expert, which tokens route there (bitmaps built with integer atomics, whose
-// result does not depend on order); a second pass reduces each (chunk, expert,
-// 128-column tile) with 16 waves that each own a fixed slice of the chunk's
-// rows, combined in wave order; a last pass adds the chunk partials to the
-// running sums in chunk order.  The sums therefore repeat bit for bit, and no
-// x^2 temporary of the activation's size is ever materialised.
+// result does not depend on order); a second pass reduces each (slice of a
+// chunk, expert, 512-column tile) with 4 waves that take the slice's member
+// tokens in turn (member m to wave m mod 4, each wave in token order, 8 rows per
+// load batch of 16-byte loads), the wave partials combined in wave order; a
+// last pass adds the slice partials to the running sums in slice order (chunk
+// by chunk).  The sums therefore repeat bit for bit, and no x^2 temporary of
+// the activation's size is ever materialised.
 
 #include <type_traits>
 
@@ -27,20 +29,28 @@
 
 namespace iq {
 
-// Pass 1 (routed): membership bitmaps bm[chunk][e][words] and counts.
+// Pass 1 (routed): membership bitmaps bm[chunk][e][words] and counts.  One
+// workgroup per 256 positions of a chunk: it clears its own 8 words of every
+// expert's row (the chunk's last workgroup also the row's tail), then marks.
 __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__restrict__ ids, int64_t T,
                                                              int top_k, int E, int chunk_rows, int W,
                                                              uint32_t *__restrict__ bm,
                                                              int64_t *__restrict__ counts,
                                                              int32_t *status) {
-  const int64_t chunk = blockIdx.x;
+  const int nsub = (chunk_rows + 255) / 256;
+  const int64_t chunk = blockIdx.x / nsub;
+  const int sub = static_cast<int>(blockIdx.x % nsub);
   uint32_t *reg = bm + chunk * static_cast<int64_t>(E) * W;
-  for (int64_t i = threadIdx.x; i < static_cast<int64_t>(E) * W; i += blockDim.x) reg[i] = 0u;
+  const int w0 = sub * 8;
+  const int w1 = sub == nsub - 1 ? W : w0 + 8;
+  for (int64_t i = threadIdx.x; i < static_cast<int64_t>(E) * (w1 - w0); i += blockDim.x)
+    reg[(i / (w1 - w0)) * W + w0 + i % (w1 - w0)] = 0u;
   __syncthreads();
   const int64_t t0 = chunk * chunk_rows;
   const int64_t n = (T - t0 < chunk_rows) ? (T - t0) : chunk_rows;
+  const int64_t p = static_cast<int64_t>(sub) * 256 + threadIdx.x;
   int st = 0;
-  for (int64_t p = threadIdx.x; p < n; p += blockDim.x) {
+  if (p < n) {
     for (int s = 0; s < top_k; ++s) {
       const int e = ids[(t0 + p) * top_k + s];
       if (e < 0 || e >= E) { st |= ST_BADID; continue; }
@@ -51,108 +61,138 @@ __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__res
   raise_status(status, st);
 }
 
-// Pass 2: partial[chunk][e][K] = sum over the chunk's rows routed to e of x^2.
-// Workgroup = 16 waves x 64 lanes over a 128-column tile; lane owns 2 columns;
-// wave w owns rows [w * rpw, (w + 1) * rpw) of the chunk and adds them in row
-// order, loading 16 rows per batch; the 16 wave partials are then added in wave
-// order.
-constexpr int kTile = 128, kBatch = 16;
+// Pass 2: partial[slice][e][K] = sum over the slice's member tokens (routed to
+// e; dense: all) of x^2.  Workgroup = 4 waves over a 512-column tile, 8 columns
+// per lane; member m of the slice (ascending tokens, a token routed twice to e
+// counted twice) goes to wave m mod 4.
+constexpr int kCPL = 8, kCTile = 64 * kCPL, kCWaves = 4, kCBatch = 8;
 
-template <int DT, bool PAIR>
-__global__ void __launch_bounds__(1024) collect_partial_kernel(const void *__restrict__ x, int64_t T, int64_t K,
-                                                                const int32_t *__restrict__ ids, int top_k,
-                                                                int E, int chunk_rows, int W,
-                                                                const uint32_t *__restrict__ bm,
-                                                                float *__restrict__ partial, int32_t *status) {
-  __shared__ float s_part[16][kTile];
-  const int64_t ntile = (K + kTile - 1) / kTile;
+template <int DT, bool VEC>
+__global__ void __launch_bounds__(64 * kCWaves) collect_slice_kernel(const void *__restrict__ x, int64_t T,
+                                                                      int64_t K, const int32_t *__restrict__ ids,
+                                                                      int top_k, int E, int chunk_rows, int W,
+                                                                      const uint32_t *__restrict__ bm, int nsub,
+                                                                      int slice_len, float *__restrict__ partial,
+                                                                      int32_t *status) {
+  __shared__ float s_acc[kCWaves][kCTile];
+  const int64_t ntile = (K + kCTile - 1) / kCTile;
   const int64_t tile = blockIdx.x % ntile;
-  const int64_t ce = blockIdx.x / ntile;  // chunk * E + e
-  const int e = static_cast<int>(ce % E);
-  const int64_t chunk = ce / E;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: row bookkeeping stays scalar
+  const int64_t rest = blockIdx.x / ntile;  // slice * E + e
+  const int e = static_cast<int>(rest % E);
+  const int64_t slice = rest / E;
+  const int64_t chunk = slice / nsub;
+  const int sub = static_cast<int>(slice % nsub);
+  const int64_t cbase = chunk * chunk_rows;
+  const int64_t n = (T - cbase < chunk_rows) ? (T - cbase) : chunk_rows;
+  const int64_t p_lo = static_cast<int64_t>(sub) * slice_len;
+  const int64_t p_hi = (p_lo + slice_len < n) ? p_lo + slice_len : n;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: token bookkeeping stays scalar
   const int lane = threadIdx.x & 63;
-  const int64_t t0 = chunk * chunk_rows;
-  const int64_t n = (T - t0 < chunk_rows) ? (T - t0) : chunk_rows;
-  const int64_t rpw = (((chunk_rows + 15) / 16) + 63) / 64 * 64;  // rows per wave, whole 64-row words
-  const int64_t cl = tile * kTile + lane * 2;             // this lane's first column
+  const int64_t col = tile * kCTile + lane * kCPL;
   // lanes past the last column read a valid column and their results are dropped
-  const int64_t c0 = cl < K ? cl : (PAIR ? K - 2 : K - 1);
-  float acc0 = 0.0f, acc1 = 0.0f;
+  const int64_t colv = VEC ? (col < K ? col : K - kCPL) : col;
+  const uint32_t *words = ids ? bm + (chunk * E + e) * W : nullptr;
+
+  float acc[kCPL];
+#pragma unroll
+  for (int j = 0; j < kCPL; ++j) acc[j] = 0.0f;
   bool finite = true;
-  for (int64_t base = wave * rpw; base < (wave + 1) * rpw && base < n; base += 64) {
-    const int64_t cnt = (n - base < 64) ? (n - base) : 64;
-    const uint64_t live = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
-    uint64_t mm = live;
-    if (ids) {
-      const uint32_t *wrow = bm + ce * W;
-      const uint64_t lo = wrow[base >> 5];
-      const uint64_t hi = ((base >> 5) + 1 < W) ? wrow[(base >> 5) + 1] : 0u;
-      mm = (lo | (hi << 32)) & live;
-    }
-    while (mm) {
-      // next kBatch member rows in ascending order; empty slots reuse a valid
-      // row and contribute an exact zero, so the loads need no branches
-      int64_t tok[kBatch];
-      bool ok[kBatch];
+  // member stream (uniform): dense members are the slice's positions in order;
+  // routed members come from the bitmap words, each repeated by multiplicity
+  int64_t pos = p_lo;          // next position to examine
+  int64_t m = 0;               // members seen so far
+  uint32_t bits = 0u;          // unread bits of the current word
+  int64_t wbase = p_lo;        // position of bit 0 of the current word
+  int64_t wnext = p_lo >> 5;   // next word to read
+  while (true) {
+    int64_t tok[kCBatch];
+    int mult[kCBatch];
+    int nt = 0;
+    if (!ids) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        ok[u] = mm != 0;
-        tok[u] = t0 + base + (ok[u] ? __builtin_ctzll(mm) : 0);
-        mm &= mm - 1;
+      for (int u = 0; u < kCBatch; ++u) {
+        const int64_t q = pos + wave + static_cast<int64_t>(u) * kCWaves;
+        mult[u] = q < p_hi ? 1 : 0;
+        tok[u] = cbase + (q < p_hi ? q : p_lo);
+        nt += mult[u];
       }
-      float v0[kBatch], v1[kBatch];
+      pos += static_cast<int64_t>(kCBatch) * kCWaves;
+    } else {
+      while (nt < kCBatch) {
+        if (bits == 0u) {
+          if ((wnext << 5) >= p_hi) break;
+          wbase = wnext << 5;
+          bits = words[wnext];
+          ++wnext;
+          continue;
+        }
+        const int64_t q = wbase + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        if (q >= p_hi) { bits = 0u; continue; }
+        if (m++ % kCWaves != wave) continue;
+        int c = 0;
+        for (int s2 = 0; s2 < top_k; ++s2) c += ids[(cbase + q) * top_k + s2] == e;
+        tok[nt] = cbase + q;
+        mult[nt] = c;
+        ++nt;
+      }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int64_t off = tok[u] * K + c0;
-        if (PAIR) {  // even K: one 2-column load
-          if (DT == 1) {
-            const uint32_t q = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(x) + off);
-            v0[u] = __uint_as_float(q << 16);
-            v1[u] = __uint_as_float(q & 0xffff0000u);
-          } else {
-            const float2 q = *reinterpret_cast<const float2 *>(static_cast<const float *>(x) + off);
-            v0[u] = q.x;
-            v1[u] = q.y;
+      for (int u = 0; u < kCBatch; ++u)
+        if (u >= nt) { tok[u] = cbase + p_lo; mult[u] = 0; }
+    }
+    if (nt == 0) break;
+    float v[kCBatch][kCPL];
+#pragma unroll
+    for (int u = 0; u < kCBatch; ++u) {
+      const int64_t off = tok[u] * K + colv;
+      if (VEC) {
+        if (DT == 1) {
+          const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+          const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            v[u][2 * h] = __uint_as_float(qq[h] << 16);
+            v[u][2 * h + 1] = __uint_as_float(qq[h] & 0xffff0000u);
           }
         } else {
-          const int64_t o1 = (c0 + 1 < K) ? off + 1 : off;
-          v0[u] = DT == 1 ? bf16_to_f32(static_cast<const uint16_t *>(x)[off]) : static_cast<const float *>(x)[off];
-          v1[u] = DT == 1 ? bf16_to_f32(static_cast<const uint16_t *>(x)[o1]) : static_cast<const float *>(x)[o1];
+          const float4 q0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
+          const float4 q1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off + 4);
+          v[u][0] = q0.x; v[u][1] = q0.y; v[u][2] = q0.z; v[u][3] = q0.w;
+          v[u][4] = q1.x; v[u][5] = q1.y; v[u][6] = q1.z; v[u][7] = q1.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kCPL; ++j) {
+          const int64_t c = col + j < K ? off + j : tok[u] * K + (K - 1);
+          v[u][j] = DT == 1 ? bf16_to_f32(static_cast<const uint16_t *>(x)[c]) : static_cast<const float *>(x)[c];
         }
       }
+    }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        int mult = ok[u] ? 1 : 0;
-        if (ids && ok[u]) {  // multiplicity of e in this token's top-k (usually 1)
-          mult = 0;
-          for (int s2 = 0; s2 < top_k; ++s2) mult += ids[tok[u] * top_k + s2] == e;
-        }
-        const float a0 = mult ? v0[u] : 0.0f, a1 = mult ? v1[u] : 0.0f;
-        finite = finite && finite_f(a0) && finite_f(a1);
-        acc0 = __builtin_fmaf(a0, a0, acc0);
-        acc1 = __builtin_fmaf(a1, a1, acc1);
-        for (int rep = 1; rep < mult; ++rep) {
-          acc0 = __builtin_fmaf(a0, a0, acc0);
-          acc1 = __builtin_fmaf(a1, a1, acc1);
+    for (int u = 0; u < kCBatch; ++u) {
+      for (int rep = 0; rep < mult[u]; ++rep) {
+#pragma unroll
+        for (int j = 0; j < kCPL; ++j) {
+          if (col + j < K) finite = finite && finite_f(v[u][j]);
+          acc[j] = __builtin_fmaf(v[u][j], v[u][j], acc[j]);
         }
       }
     }
   }
-  s_part[wave][lane * 2] = acc0;
-  s_part[wave][lane * 2 + 1] = acc1;
+#pragma unroll
+  for (int j = 0; j < kCPL; ++j) s_acc[wave][lane * kCPL + j] = acc[j];
   if (!finite) raise_status(status, ST_NONFINITE);
   __syncthreads();
-  if (threadIdx.x < kTile) {  // columns past K (clamped lanes) are not stored
-    const int64_t col = tile * kTile + threadIdx.x;
-    float p = s_part[0][threadIdx.x];
+  for (int c = threadIdx.x; c < kCTile; c += blockDim.x) {
+    const int64_t cc = tile * kCTile + c;
+    float p = s_acc[0][c];
 #pragma unroll
-    for (int w = 1; w < 16; ++w) p = p + s_part[w][threadIdx.x];
-    if (col < K) partial[ce * K + col] = p;
+    for (int w = 1; w < kCWaves; ++w) p = p + s_acc[w][c];
+    if (cc < K) partial[rest * K + cc] = p;
   }
 }
 
-// Pass 3: sums[e][j] += partial[0][e][j]; += partial[1][e][j]; ... (chunk order)
+// Pass 3: sums[e][j] += partial[0][e][j]; += partial[1][e][j]; ... (slice order)
 __global__ void __launch_bounds__(256) collect_combine_kernel(const float *__restrict__ partial, int64_t nchunks,
                                                                int64_t EK, float *__restrict__ sums,
                                                                int64_t *counts, int64_t dense_T) {
@@ -168,34 +208,43 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
                    int chunk_rows, float *sums, int64_t *counts, int32_t *status, hipStream_t stream) {
   if (T == 0) return 0;
   const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
-  const int W = (chunk_rows + 31) / 32 + 1;  // +1: a 64-bit read past the last word stays in the row
+  const int W = (chunk_rows + 31) / 32 + 1;
+  const int64_t ntile = (K + kCTile - 1) / kCTile;
+  // slices of a chunk (whole 32-position words) so the launch has >= 512 workgroups
+  int64_t nsub = (512 + nchunks * E * ntile - 1) / (nchunks * E * ntile);
+  const int64_t max_sub = (chunk_rows + 31) / 32;
+  if (nsub > max_sub) nsub = max_sub;
+  if (nsub < 1) nsub = 1;
+  const int64_t slice_len = ((chunk_rows + nsub - 1) / nsub + 31) / 32 * 32;
+  nsub = (chunk_rows + slice_len - 1) / slice_len;
+  const int64_t nslices = nchunks * nsub;
   const int64_t EK = static_cast<int64_t>(E) * K;
-  const size_t pbytes = static_cast<size_t>(nchunks) * EK * sizeof(float);
+  const size_t pbytes = static_cast<size_t>(nslices) * EK * sizeof(float);
   const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
   void *scratch = nullptr;
   if (hipMallocAsync(&scratch, pbytes + bbytes + 256, stream) != hipSuccess) return -1;
   float *partial = static_cast<float *>(scratch);
   uint32_t *bm = reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + ((pbytes + 255) & ~size_t(255)));
   if (ids)
-    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks)), dim3(256), 0, stream, ids, T,
-                       top_k, E, chunk_rows, W, bm, counts, status);
-  const int64_t ntile = (K + kTile - 1) / kTile;
-  const dim3 g2(static_cast<unsigned>(nchunks * E * ntile));
-  const bool pair = (K & 1) == 0;
-  if (dtype == 1 && pair)
-    hipLaunchKernelGGL((collect_partial_kernel<1, true>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
-                       chunk_rows, W, bm, partial, status);
+    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, counts, status);
+  const dim3 g2(static_cast<unsigned>(nslices * E * ntile));
+  const bool vec = K % kCPL == 0;  // 16-byte (bf16) / 32-byte (f32) aligned rows, whole 8-column lanes
+  const int ns = static_cast<int>(nsub), sl = static_cast<int>(slice_len);
+  if (dtype == 1 && vec)
+    hipLaunchKernelGGL((collect_slice_kernel<1, true>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k, E,
+                       chunk_rows, W, bm, ns, sl, partial, status);
   else if (dtype == 1)
-    hipLaunchKernelGGL((collect_partial_kernel<1, false>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
-                       chunk_rows, W, bm, partial, status);
-  else if (pair)
-    hipLaunchKernelGGL((collect_partial_kernel<0, true>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
-                       chunk_rows, W, bm, partial, status);
+    hipLaunchKernelGGL((collect_slice_kernel<1, false>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k,
+                       E, chunk_rows, W, bm, ns, sl, partial, status);
+  else if (vec)
+    hipLaunchKernelGGL((collect_slice_kernel<0, true>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k, E,
+                       chunk_rows, W, bm, ns, sl, partial, status);
   else
-    hipLaunchKernelGGL((collect_partial_kernel<0, false>), g2, dim3(1024), 0, stream, x, T, K, ids, top_k, E,
-                       chunk_rows, W, bm, partial, status);
+    hipLaunchKernelGGL((collect_slice_kernel<0, false>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k,
+                       E, chunk_rows, W, bm, ns, sl, partial, status);
   hipLaunchKernelGGL(collect_combine_kernel, dim3(static_cast<unsigned>((EK + 255) / 256)), dim3(256), 0, stream,
-                     partial, nchunks, EK, sums, counts, ids ? int64_t(0) : T);
+                     partial, nslices, EK, sums, counts, ids ? int64_t(0) : T);
   const hipError_t le = hipGetLastError();
   hipFreeAsync(scratch, stream);
   return le == hipSuccess ? 0 : -1;
@@ -541,8 +590,8 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + off_b) : nullptr;
   int64_t *cnt = ids ? reinterpret_cast<int64_t *>(static_cast<char *>(scratch) + off_c) : nullptr;
   if (ids)
-    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks)), dim3(256), 0, stream, ids, T,
-                       top_k, E, chunk_rows, W, bm, cnt, status);
+    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, cnt, status);
   float *dst = nsplit > 1 ? partial : hess;
   const bool accumulate = nsplit == 1;
   const dim3 g(static_cast<unsigned>(ntiles * nsplit));

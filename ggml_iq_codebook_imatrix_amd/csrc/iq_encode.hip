@@ -430,7 +430,7 @@ __device__ __forceinline__ void stage_grid(const float *__restrict__ grid, float
 enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2, RECORDS = 3 };
 
 template <int F, int MODE>
-__global__ void __launch_bounds__(64 * Geo<F>::WGG, 4) search_kernel(EncArgs A) {
+__global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   using G = Geo<F>;
   constexpr bool FIXED = MODE == FIXED_CHOICES;
   constexpr int WGG = G::WGG, GPU = G::GPU, N = G::N;
@@ -441,10 +441,12 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, 4) search_kernel(EncArgs A) 
   // fixed choices: one slot (IQ1_M: its two shifts)
   constexpr int NSLOT = FIXED ? (F == IQ1_M ? 2 : 1) : 16;
 
-  // s_u: the per-slot minima exchanged for scoring (search), then, for the IQ2
-  // layouts, the grid copy the rescans read
+  // s_u: the per-slot minima exchanged for scoring (search), or, for the IQ2
+  // layouts' every-choice sweeps (16 rescans per lane), the grid copy the
+  // rescans read
+  constexpr bool LDS_RESCAN = !G::IQ1 && (MODE == EVERY || MODE == RECORDS);
   constexpr int BEST_F = MODE == SEARCH ? WGG * NSLOT * 64 : 1;
-  constexpr int GRID_F = G::IQ1 ? 1 : N * 8 + (N / 32) * 4;
+  constexpr int GRID_F = LDS_RESCAN ? N * 8 + (N / 32) * 4 : 1;
   __shared__ __attribute__((aligned(16))) float s_u[BEST_F > GRID_F ? BEST_F : GRID_F];
   float (*s_best)[NSLOT][64] = reinterpret_cast<float (*)[NSLOT][64]>(s_u);
   __shared__ uint16_t s_k[WGG][64];
@@ -571,7 +573,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, 4) search_kernel(EncArgs A) 
   }
 
   // ---- every choice: one field record per choice and group ----------------
-  if (!G::IQ1 && MODE != SEARCH) stage_grid<N>(A.grid, s_u);
+  if (LDS_RESCAN) stage_grid<N>(A.grid, s_u);
   if (MODE == RECORDS) {
     uint32_t *rp = A.rec + (static_cast<int64_t>(b) * 32 + gi) * A.rows + r;
     const int64_t cstride = static_cast<int64_t>(A.nb) * 32 * A.rows;
@@ -584,8 +586,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, 4) search_kernel(EncArgs A) 
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (G::IQ1) rescan_chunk<F>(A.grid, gt, S, chs, ssel, slot >> 3, kb, mfield);
-      else rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
+      else rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
       GroupFields f;
       f.d16 = d16;
       f.k = static_cast<uint32_t>(kb);
@@ -609,8 +611,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, 4) search_kernel(EncArgs A) 
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (G::IQ1) rescan_chunk<F>(A.grid, gt, S, chs, ssel, slot >> 3, kb, mfield);
-      else rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
+      else rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
       int cu = c;
       if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
       __syncthreads();  // the previous choice's bytes have been read from LDS
@@ -693,13 +695,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, 4) search_kernel(EncArgs A) 
   }
   int kb;
   uint32_t mfield;
-  if (G::IQ1) {
-    rescan_chunk<F>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
-  } else {
-    if (MODE == SEARCH) __syncthreads();  // every wave has read the minima
-    stage_grid<N>(A.grid, s_u);
-    rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
-  }
+  rescan_chunk<F>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
   if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
 
   // ---- pack ----------------------------------------------------------------
