@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__res
                                                              int top_k, int E, int chunk_rows, int W,
                                                              uint32_t *__restrict__ bm,
                                                              int64_t *__restrict__ counts,
-                                                             int32_t *status) {
+                                                             uint8_t *__restrict__ dup, int32_t *status) {
   const int nsub = (chunk_rows + 255) / 256;
   const int64_t chunk = blockIdx.x / nsub;
   const int sub = static_cast<int>(blockIdx.x % nsub);
@@ -51,30 +51,39 @@ __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__res
   const int64_t p = static_cast<int64_t>(sub) * 256 + threadIdx.x;
   int st = 0;
   if (p < n) {
+    bool rep = false;  // an expert named twice by this token
     for (int s = 0; s < top_k; ++s) {
       const int e = ids[(t0 + p) * top_k + s];
       if (e < 0 || e >= E) { st |= ST_BADID; continue; }
+      for (int s2 = 0; s2 < s; ++s2) rep = rep || ids[(t0 + p) * top_k + s2] == e;
       atomicOr(&reg[static_cast<int64_t>(e) * W + (p >> 5)], 1u << (p & 31));
       atomicAdd(reinterpret_cast<unsigned long long *>(counts + e), 1ull);
     }
+    if (dup) dup[t0 + p] = rep ? 1 : 0;
   }
   raise_status(status, st);
 }
 
 // Pass 2: partial[slice][e][K] = sum over the slice's member tokens (routed to
-// e; dense: all) of x^2.  Workgroup = 4 waves over a 512-column tile, 8 columns
-// per lane; member m of the slice (ascending tokens, a token routed twice to e
-// counted twice) goes to wave m mod 4.
-constexpr int kCPL = 8, kCTile = 64 * kCPL, kCWaves = 4, kCBatch = 8;
+// e; dense: all) of x^2.  Workgroup = NW waves over a 512-column tile, 8
+// columns per lane; member m of the slice (ascending tokens, a token routed
+// twice to e counted twice) goes to wave m mod NW, which adds its members in
+// token order, 8 rows per batch of 16-byte loads.  Routed slices (at most 1,024
+// positions) first list their members in LDS from the bitmap words, one word
+// per lane.
+constexpr int kCPL = 8, kCTile = 64 * kCPL, kCBatch = 8, kMaxRoutedSlice = 1024;
 
-template <int DT, bool VEC>
-__global__ void __launch_bounds__(64 * kCWaves) collect_slice_kernel(const void *__restrict__ x, int64_t T,
-                                                                      int64_t K, const int32_t *__restrict__ ids,
-                                                                      int top_k, int E, int chunk_rows, int W,
-                                                                      const uint32_t *__restrict__ bm, int nsub,
-                                                                      int slice_len, float *__restrict__ partial,
-                                                                      int32_t *status) {
-  __shared__ float s_acc[kCWaves][kCTile];
+template <int DT, bool VEC, int NW, bool ROUTED>
+__global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__restrict__ x, int64_t T, int64_t K,
+                                                                 const int32_t *__restrict__ ids, int top_k, int E,
+                                                                 int chunk_rows, int W,
+                                                                 const uint32_t *__restrict__ bm,
+                                                                 const uint8_t *__restrict__ dup, int nsub,
+                                                                 int slice_len, float *__restrict__ partial,
+                                                                 int32_t *status) {
+  __shared__ float s_acc[NW][kCTile];
+  __shared__ int s_mem[ROUTED ? kMaxRoutedSlice : 1];
+  __shared__ int s_nmem;
   const int64_t ntile = (K + kCTile - 1) / kCTile;
   const int64_t tile = blockIdx.x % ntile;
   const int64_t rest = blockIdx.x / ntile;  // slice * E + e
@@ -91,56 +100,61 @@ __global__ void __launch_bounds__(64 * kCWaves) collect_slice_kernel(const void 
   const int64_t col = tile * kCTile + lane * kCPL;
   // lanes past the last column read a valid column and their results are dropped
   const int64_t colv = VEC ? (col < K ? col : K - kCPL) : col;
-  const uint32_t *words = ids ? bm + (chunk * E + e) * W : nullptr;
+
+  int64_t nmem = p_hi > p_lo ? p_hi - p_lo : 0;  // dense: the positions themselves
+  if (ROUTED) {
+    if (wave == 0) {
+      // lane l lists the members in word l of the slice: positions p_lo + 32 l + bit
+      const int64_t nw = (nmem + 31) / 32;
+      uint32_t word = 0u;
+      if (lane < nw) {
+        word = bm[(chunk * E + e) * W + (p_lo >> 5) + lane];
+        const int64_t lim = nmem - 32 * static_cast<int64_t>(lane);
+        if (lim < 32) word &= (1u << lim) - 1u;
+      }
+      const int cnt = __builtin_popcount(word);
+      int pre = cnt;  // inclusive prefix over lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(pre, d);
+        if (lane >= d) pre += o;
+      }
+      int at = pre - cnt;
+      while (word) {
+        s_mem[at++] = static_cast<int>(p_lo + 32 * lane + __builtin_ctz(word));
+        word &= word - 1u;
+      }
+      if (lane == 63) s_nmem = pre;
+    }
+    __syncthreads();
+    nmem = s_nmem;
+  }
 
   float acc[kCPL];
 #pragma unroll
   for (int j = 0; j < kCPL; ++j) acc[j] = 0.0f;
   bool finite = true;
-  // member stream (uniform): dense members are the slice's positions in order;
-  // routed members come from the bitmap words, each repeated by multiplicity
-  int64_t pos = p_lo;          // next position to examine
-  int64_t m = 0;               // members seen so far
-  uint32_t bits = 0u;          // unread bits of the current word
-  int64_t wbase = p_lo;        // position of bit 0 of the current word
-  int64_t wnext = p_lo >> 5;   // next word to read
-  while (true) {
+  for (int64_t m0 = wave; m0 < nmem; m0 += static_cast<int64_t>(NW) * kCBatch) {
     int64_t tok[kCBatch];
     int mult[kCBatch];
-    int nt = 0;
-    if (!ids) {
+#pragma unroll
+    for (int u = 0; u < kCBatch; ++u) {
+      const int64_t mi = m0 + static_cast<int64_t>(u) * NW;
+      const bool ok = mi < nmem;
+      const int64_t q = ok ? (ROUTED ? s_mem[mi] : p_lo + mi) : (ROUTED ? s_mem[0] : p_lo);
+      tok[u] = cbase + q;
+      mult[u] = ok ? 1 : 0;
+    }
+    if (ROUTED) {
 #pragma unroll
       for (int u = 0; u < kCBatch; ++u) {
-        const int64_t q = pos + wave + static_cast<int64_t>(u) * kCWaves;
-        mult[u] = q < p_hi ? 1 : 0;
-        tok[u] = cbase + (q < p_hi ? q : p_lo);
-        nt += mult[u];
-      }
-      pos += static_cast<int64_t>(kCBatch) * kCWaves;
-    } else {
-      while (nt < kCBatch) {
-        if (bits == 0u) {
-          if ((wnext << 5) >= p_hi) break;
-          wbase = wnext << 5;
-          bits = words[wnext];
-          ++wnext;
-          continue;
+        if (mult[u] && dup[tok[u]]) {  // rare: count the repeats of e in this token's ids
+          int c = 0;
+          for (int s2 = 0; s2 < top_k; ++s2) c += ids[tok[u] * top_k + s2] == e;
+          mult[u] = c;
         }
-        const int64_t q = wbase + __builtin_ctz(bits);
-        bits &= bits - 1u;
-        if (q >= p_hi) { bits = 0u; continue; }
-        if (m++ % kCWaves != wave) continue;
-        int c = 0;
-        for (int s2 = 0; s2 < top_k; ++s2) c += ids[(cbase + q) * top_k + s2] == e;
-        tok[nt] = cbase + q;
-        mult[nt] = c;
-        ++nt;
       }
-#pragma unroll
-      for (int u = 0; u < kCBatch; ++u)
-        if (u >= nt) { tok[u] = cbase + p_lo; mult[u] = 0; }
     }
-    if (nt == 0) break;
     float v[kCBatch][kCPL];
 #pragma unroll
     for (int u = 0; u < kCBatch; ++u) {
@@ -187,7 +201,7 @@ __global__ void __launch_bounds__(64 * kCWaves) collect_slice_kernel(const void 
     const int64_t cc = tile * kCTile + c;
     float p = s_acc[0][c];
 #pragma unroll
-    for (int w = 1; w < kCWaves; ++w) p = p + s_acc[w][c];
+    for (int w = 1; w < NW; ++w) p = p + s_acc[w][c];
     if (cc < K) partial[rest * K + cc] = p;
   }
 }
@@ -200,8 +214,24 @@ __global__ void __launch_bounds__(256) collect_combine_kernel(const float *__res
   if (i == 0 && dense_T > 0) counts[0] += dense_T;
   if (i >= EK) return;
   float s = sums[i];
-  for (int64_t c = 0; c < nchunks; ++c) s = s + partial[c * EK + i];
+  int64_t c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    float p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = partial[(c + u) * EK + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = s + p[u];
+  }
+  for (; c < nchunks; ++c) s = s + partial[c * EK + i];
   sums[i] = s;
+}
+
+template <int DT, bool VEC, int NW, bool ROUTED>
+static void launch_slices(dim3 g, hipStream_t stream, const void *x, int64_t T, int64_t K, const int32_t *ids,
+                          int top_k, int E, int chunk_rows, int W, const uint32_t *bm, const uint8_t *dup, int nsub,
+                          int slice_len, float *partial, int32_t *status) {
+  hipLaunchKernelGGL((collect_slice_kernel<DT, VEC, NW, ROUTED>), g, dim3(64 * NW), 0, stream, x, T, K, ids, top_k, E,
+                     chunk_rows, W, bm, dup, nsub, slice_len, partial, status);
 }
 
 int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
@@ -210,8 +240,12 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
   const int W = (chunk_rows + 31) / 32 + 1;
   const int64_t ntile = (K + kCTile - 1) / kCTile;
-  // slices of a chunk (whole 32-position words) so the launch has >= 512 workgroups
-  int64_t nsub = (512 + nchunks * E * ntile - 1) / (nchunks * E * ntile);
+  // dense: 16-wave workgroups, slices sized for >= 32 workgroups; routed:
+  // 4-wave workgroups, slices of at most 1,024 positions and >= 512 workgroups
+  const int64_t want = ids ? 512 : 32;
+  int64_t nsub = (want + nchunks * E * ntile - 1) / (nchunks * E * ntile);
+  if (ids && nsub < (chunk_rows + kMaxRoutedSlice - 1) / kMaxRoutedSlice)
+    nsub = (chunk_rows + kMaxRoutedSlice - 1) / kMaxRoutedSlice;
   const int64_t max_sub = (chunk_rows + 31) / 32;
   if (nsub > max_sub) nsub = max_sub;
   if (nsub < 1) nsub = 1;
@@ -221,28 +255,37 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   const int64_t EK = static_cast<int64_t>(E) * K;
   const size_t pbytes = static_cast<size_t>(nslices) * EK * sizeof(float);
   const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
+  const size_t dbytes = ids ? static_cast<size_t>(T) : 0;
+  const size_t boff = (pbytes + 255) & ~size_t(255), doff = boff + ((bbytes + 255) & ~size_t(255));
   void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, pbytes + bbytes + 256, stream) != hipSuccess) return -1;
+  if (hipMallocAsync(&scratch, doff + dbytes + 256, stream) != hipSuccess) return -1;
   float *partial = static_cast<float *>(scratch);
-  uint32_t *bm = reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + ((pbytes + 255) & ~size_t(255)));
+  uint32_t *bm = reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + boff);
+  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(static_cast<char *>(scratch) + doff) : nullptr;
   if (ids)
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
-                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, counts, status);
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, counts, dup, status);
   const dim3 g2(static_cast<unsigned>(nslices * E * ntile));
   const bool vec = K % kCPL == 0;  // 16-byte (bf16) / 32-byte (f32) aligned rows, whole 8-column lanes
   const int ns = static_cast<int>(nsub), sl = static_cast<int>(slice_len);
-  if (dtype == 1 && vec)
-    hipLaunchKernelGGL((collect_slice_kernel<1, true>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k, E,
-                       chunk_rows, W, bm, ns, sl, partial, status);
-  else if (dtype == 1)
-    hipLaunchKernelGGL((collect_slice_kernel<1, false>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k,
-                       E, chunk_rows, W, bm, ns, sl, partial, status);
-  else if (vec)
-    hipLaunchKernelGGL((collect_slice_kernel<0, true>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k, E,
-                       chunk_rows, W, bm, ns, sl, partial, status);
-  else
-    hipLaunchKernelGGL((collect_slice_kernel<0, false>), g2, dim3(64 * kCWaves), 0, stream, x, T, K, ids, top_k,
-                       E, chunk_rows, W, bm, ns, sl, partial, status);
+  const uint32_t *bmc = bm;
+  auto go = [&](auto dt, auto v, auto nw, auto r) {
+    launch_slices<decltype(dt)::value, decltype(v)::value, decltype(nw)::value, decltype(r)::value>(
+        g2, stream, x, T, K, ids, top_k, E, chunk_rows, W, bmc, dup, ns, sl, partial, status);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BT = std::true_type;
+  using BF = std::false_type;
+  using WR = std::integral_constant<int, 4>;
+  using WD = std::integral_constant<int, 16>;
+  if (ids) {
+    if (dtype == 1) { if (vec) go(I1{}, BT{}, WR{}, BT{}); else go(I1{}, BF{}, WR{}, BT{}); }
+    else { if (vec) go(I0{}, BT{}, WR{}, BT{}); else go(I0{}, BF{}, WR{}, BT{}); }
+  } else {
+    if (dtype == 1) { if (vec) go(I1{}, BT{}, WD{}, BF{}); else go(I1{}, BF{}, WD{}, BF{}); }
+    else { if (vec) go(I0{}, BT{}, WD{}, BF{}); else go(I0{}, BF{}, WD{}, BF{}); }
+  }
   hipLaunchKernelGGL(collect_combine_kernel, dim3(static_cast<unsigned>((EK + 255) / 256)), dim3(256), 0, stream,
                      partial, nslices, EK, sums, counts, ids ? int64_t(0) : T);
   const hipError_t le = hipGetLastError();
@@ -591,7 +634,8 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   int64_t *cnt = ids ? reinterpret_cast<int64_t *>(static_cast<char *>(scratch) + off_c) : nullptr;
   if (ids)
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
-                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, cnt, status);
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, cnt,
+                       static_cast<uint8_t *>(nullptr), status);
   float *dst = nsplit > 1 ? partial : hess;
   const bool accumulate = nsplit == 1;
   const dim3 g(static_cast<unsigned>(ntiles * nsplit));
