@@ -29,13 +29,13 @@
 
 namespace iq {
 
-// Pass 1 (routed): membership bitmaps bm[chunk][e][words] and counts.  One
-// workgroup per 256 positions of a chunk: it clears its own 8 words of every
-// expert's row (the chunk's last workgroup also the row's tail), then marks.
+// Pass 1 (routed): membership bitmaps bm[chunk][e][words] and a per-token flag
+// for tokens that name one expert twice.  One workgroup per 256 positions of a
+// chunk: it clears its own 8 words of every expert's row (the chunk's last
+// workgroup also the row's tail), then marks.
 __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__restrict__ ids, int64_t T,
                                                              int top_k, int E, int chunk_rows, int W,
                                                              uint32_t *__restrict__ bm,
-                                                             int64_t *__restrict__ counts,
                                                              uint8_t *__restrict__ dup, int32_t *status) {
   const int nsub = (chunk_rows + 255) / 256;
   const int64_t chunk = blockIdx.x / nsub;
@@ -57,7 +57,6 @@ __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__res
       if (e < 0 || e >= E) { st |= ST_BADID; continue; }
       for (int s2 = 0; s2 < s; ++s2) rep = rep || ids[(t0 + p) * top_k + s2] == e;
       atomicOr(&reg[static_cast<int64_t>(e) * W + (p >> 5)], 1u << (p & 31));
-      atomicAdd(reinterpret_cast<unsigned long long *>(counts + e), 1ull);
     }
     if (dup) dup[t0 + p] = rep ? 1 : 0;
   }
@@ -80,8 +79,9 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
                                                                  const uint32_t *__restrict__ bm,
                                                                  const uint8_t *__restrict__ dup, int nsub,
                                                                  int slice_len, float *__restrict__ partial,
-                                                                 int32_t *status) {
+                                                                 int64_t *__restrict__ counts, int32_t *status) {
   __shared__ float s_acc[NW][kCTile];
+  __shared__ int s_cnt[NW];
   __shared__ int s_mem[ROUTED ? kMaxRoutedSlice : 1];
   __shared__ int s_nmem;
   const int64_t ntile = (K + kCTile - 1) / kCTile;
@@ -134,6 +134,7 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
 #pragma unroll
   for (int j = 0; j < kCPL; ++j) acc[j] = 0.0f;
   bool finite = true;
+  int pairs = 0;  // routed (token, slot) pairs seen by this wave
   for (int64_t m0 = wave; m0 < nmem; m0 += static_cast<int64_t>(NW) * kCBatch) {
     int64_t tok[kCBatch];
     int mult[kCBatch];
@@ -153,6 +154,7 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
           for (int s2 = 0; s2 < top_k; ++s2) c += ids[tok[u] * top_k + s2] == e;
           mult[u] = c;
         }
+        pairs += mult[u];
       }
     }
     float v[kCBatch][kCPL];
@@ -195,8 +197,14 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
   }
 #pragma unroll
   for (int j = 0; j < kCPL; ++j) s_acc[wave][lane * kCPL + j] = acc[j];
+  if (ROUTED && lane == 0) s_cnt[wave] = pairs;
   if (!finite) raise_status(status, ST_NONFINITE);
   __syncthreads();
+  if (ROUTED && tile == 0 && threadIdx.x == 0) {  // one column tile counts the expert's pairs
+    int64_t c = 0;
+    for (int w = 0; w < NW; ++w) c += s_cnt[w];
+    if (c) atomicAdd(reinterpret_cast<unsigned long long *>(counts + e), static_cast<unsigned long long>(c));
+  }
   for (int c = threadIdx.x; c < kCTile; c += blockDim.x) {
     const int64_t cc = tile * kCTile + c;
     float p = s_acc[0][c];
@@ -229,9 +237,9 @@ __global__ void __launch_bounds__(256) collect_combine_kernel(const float *__res
 template <int DT, bool VEC, int NW, bool ROUTED>
 static void launch_slices(dim3 g, hipStream_t stream, const void *x, int64_t T, int64_t K, const int32_t *ids,
                           int top_k, int E, int chunk_rows, int W, const uint32_t *bm, const uint8_t *dup, int nsub,
-                          int slice_len, float *partial, int32_t *status) {
+                          int slice_len, float *partial, int64_t *counts, int32_t *status) {
   hipLaunchKernelGGL((collect_slice_kernel<DT, VEC, NW, ROUTED>), g, dim3(64 * NW), 0, stream, x, T, K, ids, top_k, E,
-                     chunk_rows, W, bm, dup, nsub, slice_len, partial, status);
+                     chunk_rows, W, bm, dup, nsub, slice_len, partial, counts, status);
 }
 
 int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
@@ -264,14 +272,14 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(static_cast<char *>(scratch) + doff) : nullptr;
   if (ids)
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
-                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, counts, dup, status);
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, dup, status);
   const dim3 g2(static_cast<unsigned>(nslices * E * ntile));
   const bool vec = K % kCPL == 0;  // 16-byte (bf16) / 32-byte (f32) aligned rows, whole 8-column lanes
   const int ns = static_cast<int>(nsub), sl = static_cast<int>(slice_len);
   const uint32_t *bmc = bm;
   auto go = [&](auto dt, auto v, auto nw, auto r) {
     launch_slices<decltype(dt)::value, decltype(v)::value, decltype(nw)::value, decltype(r)::value>(
-        g2, stream, x, T, K, ids, top_k, E, chunk_rows, W, bmc, dup, ns, sl, partial, status);
+        g2, stream, x, T, K, ids, top_k, E, chunk_rows, W, bmc, dup, ns, sl, partial, counts, status);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -624,17 +632,15 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   nsplit = (T + split_len - 1) / split_len;
   const int64_t hn = static_cast<int64_t>(E) * (K / 256) * 65536;
   const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
-  const size_t cbytes = ids ? static_cast<size_t>(E) * sizeof(int64_t) : 0;
   const size_t pbytes = nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0;
   void *scratch = nullptr;
-  const size_t off_b = (pbytes + 255) & ~size_t(255), off_c = off_b + ((bbytes + 255) & ~size_t(255));
-  if (off_c + cbytes > 0 && hipMallocAsync(&scratch, off_c + cbytes + 256, stream) != hipSuccess) return -1;
+  const size_t off_b = (pbytes + 255) & ~size_t(255);
+  if (off_b + bbytes > 0 && hipMallocAsync(&scratch, off_b + bbytes + 256, stream) != hipSuccess) return -1;
   float *partial = static_cast<float *>(scratch);
   uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + off_b) : nullptr;
-  int64_t *cnt = ids ? reinterpret_cast<int64_t *>(static_cast<char *>(scratch) + off_c) : nullptr;
   if (ids)
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
-                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, cnt,
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm,
                        static_cast<uint8_t *>(nullptr), status);
   float *dst = nsplit > 1 ? partial : hess;
   const bool accumulate = nsplit == 1;

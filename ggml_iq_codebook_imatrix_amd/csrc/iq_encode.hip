@@ -156,6 +156,13 @@ __global__ void __launch_bounds__(256) anchor_kernel(EncArgs A, const uint8_t *_
 // IQ2: G_k = sum_j a_j g_kj^2;  IQ1: G^h_k = sum_j a_j (g_kj + delta_h)^2.
 // Thread per (table, entry).  Flat weights use a single table (a_j = 1).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void load_entry(const float *p, float g[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+  g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+}
+
 template <int F>
 __global__ void __launch_bounds__(256) gterm_kernel(const float *__restrict__ grid,
                                                      const float *__restrict__ imp, int64_t cols,
@@ -164,13 +171,14 @@ __global__ void __launch_bounds__(256) gterm_kernel(const float *__restrict__ gr
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= ntab * G::N) return;
   const int k = static_cast<int>(i % G::N);
-  const int64_t tab = i / G::N;  // = e * (cols / 8) + cg
+  // N is a multiple of the block size, so a block lies in one table: the
+  // importance values are wave-uniform
+  static_assert(G::N % 256 == 0, "a 256-thread block covers entries of one table");
+  const int64_t tab = static_cast<int64_t>(blockIdx.x) * blockDim.x / G::N;  // = e * (cols / 8) + cg
   float a[8], g[8];
+  load_entry(grid + static_cast<int64_t>(k) * 8, g);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    a[j] = imp ? imp[tab * 8 + j] : 1.0f;  // importance row e, columns 8cg..8cg+7
-    g[j] = grid[static_cast<int64_t>(k) * 8 + j];
-  }
+  for (int j = 0; j < 8; ++j) a[j] = imp ? imp[tab * 8 + j] : 1.0f;  // importance row e, columns 8cg..8cg+7
   if (!G::IQ1) {
     float s = 0.0f;
 #pragma unroll
@@ -260,12 +268,6 @@ __device__ __forceinline__ float to_vgpr(float s) {
   return v;
 }
 
-__device__ __forceinline__ void load_entry(const float *p, float g[8]) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-  g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
-  g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
-}
 
 // ---------------------------------------------------------------------------
 // Rescan one 32-entry chunk under one (scale, shift) slot: the first entry with
