@@ -39,9 +39,11 @@ GRID_SEED = {"IQ2_XXS": 201, "IQ2_XS": 202, "IQ2_S": 203, "IQ1_S": 204, "IQ1_M":
 
 
 def source_hash() -> str:
+    """Hash of the sources the search kernel is built from (the kernel the
+    roofline line reports); stored traffic figures are used only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ggml_iq_codebook_imatrix_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ("iq_common.hpp", "iq_internal.hpp", "iq_encode.hip"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

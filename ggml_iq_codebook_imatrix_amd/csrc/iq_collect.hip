@@ -248,9 +248,12 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
   const int W = (chunk_rows + 31) / 32 + 1;
   const int64_t ntile = (K + kCTile - 1) / kCTile;
-  // dense: 16-wave workgroups, slices sized for >= 32 workgroups; routed:
+  // dense: 16-wave workgroups, slices sized for >= 128 workgroups; routed:
   // 4-wave workgroups, slices of at most 1,024 positions and >= 512 workgroups
-  const int64_t want = ids ? 512 : 32;
+#ifndef IQ_COLLECT_DENSE_WGS
+#define IQ_COLLECT_DENSE_WGS 128
+#endif
+  const int64_t want = ids ? 512 : IQ_COLLECT_DENSE_WGS;
   int64_t nsub = (want + nchunks * E * ntile - 1) / (nchunks * E * ntile);
   if (ids && nsub < (chunk_rows + kMaxRoutedSlice - 1) / kMaxRoutedSlice)
     nsub = (chunk_rows + kMaxRoutedSlice - 1) / kMaxRoutedSlice;
