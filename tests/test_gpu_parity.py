@@ -158,14 +158,20 @@ def test_every_choice_parity(api, orc, fmt):
     assert not every[:, 5, 0].any()
 
 
+def _oracle_importance(orc, x, ids=None, E=1):
+    """The oracle's statistics and importance (fp32 sums, as the GPU path keeps them)."""
+    s_o, c_o, _ = orc.collect(x) if ids is None else orc.collect(x, ids, E)
+    imp_o, _ = orc.importance(s_o.astype(np.float32), c_o)
+    return s_o, c_o, imp_o
+
+
 def test_every_choice_full_size_sampled(api, orc):
     say("every choice full size IQ2_XS")
     w, x, grid, spec = inputs.workload("iq2_xs_5632x2048")
-    sums, counts = api.imatrix_collect(dev_w(x, "bf16"), chunk_rows=1024)
-    imp = api.imatrix_importance(sums, counts)
-    every = host(api.quantize_every_choice("IQ2_XS", dev_w(w, "bf16"), dev(grid), imp))
+    _, _, imp = _oracle_importance(orc, x)
+    every = host(api.quantize_every_choice("IQ2_XS", dev_w(w, "bf16"), dev(grid), dev(imp)))
     rid = np.sort(inputs.rng(2200).choice(w.shape[0], 12, replace=False))
-    want, _ = orc.quantize_every_choice("IQ2_XS", w, grid, host(imp), row_ids=rid)
+    want, _ = orc.quantize_every_choice("IQ2_XS", w, grid, imp, row_ids=rid)
     assert np.array_equal(every[:, rid], want)
 
 
@@ -206,6 +212,26 @@ def test_choice_search_parity(api, orc, fmt):
     p = host(api.quantize(fmt, dev_w(w, "bf16"), dev(grid), dev(imp), rows_per_expert=rpe, choices=dev(got)))
     pw, _ = orc.quantize(fmt, w, grid, imp, rows_per_expert=rpe, choices=want)
     assert np.array_equal(p, pw)
+
+
+@pytest.mark.parametrize("fmt", ["IQ2_XS", "IQ1_M"])
+def test_choice_search_full_size_sampled(api, orc, fmt):
+    """5632x2048 bf16 in the launch configuration bench.py times, with the
+    Hessian blocks of the workload's 4,096 tokens (the oracle's, rounded to
+    fp32, fed to both sides); sampled rows against the oracle."""
+    say("choice search full size", fmt)
+    w, x, _, _ = inputs.workload("iq2_xs_5632x2048")
+    grid = inputs.grid_for(fmt, GRID_SEED[fmt])
+    _, _, imp = _oracle_importance(orc, x)
+    hess64, _ = orc.hessian_collect(x)
+    hess = hess64.astype(np.float32)
+    del hess64
+    got = host(api.choice_search(fmt, dev_w(w, "bf16"), dev(grid), dev(hess), dev(imp)))
+    rid = np.sort(inputs.rng(2400).choice(w.shape[0], 8, replace=False))
+    rid[-1] = w.shape[0] - 1
+    want, _ = orc.choice_search(fmt, w, grid, hess, imp, row_ids=rid, threads=16)
+    bad = np.argwhere(got[rid] != want)
+    assert bad.size == 0, f"{len(bad)} picks differ, first {bad[:5].tolist()}"
 
 
 def test_encode_is_deterministic(api):
@@ -427,20 +453,34 @@ def test_hessian_workload_sizes(api, orc):
 
 
 # ---------------------------------------------------------------------------
-# The named workloads, end to end (GPU importance fed to both encoders)
+# The named workloads, end to end.  Each GPU stage is checked against the
+# oracle's: the GPU statistics against the oracle's sums (1e-5), the GPU
+# importance kernel on the oracle's fp32 sums bit for bit, and the encoders on
+# the oracle's importance byte for byte (the same input on both sides, so no
+# pick can flip on a last-bit difference in the statistics).
 # ---------------------------------------------------------------------------
+def _check_statistics(api, orc, sums, counts, s_o, c_o, imp_o):
+    c = host(counts)
+    assert np.array_equal(c, c_o)
+    live = c_o > 0
+    assert _rel_close(host(sums)[live], s_o[live])
+    # the importance kernel on the oracle's own fp32 sums: bit-exact
+    got = host(api.imatrix_importance(dev(s_o.astype(np.float32)), dev(c_o)))
+    assert np.array_equal(got.view(np.uint32), imp_o.view(np.uint32))
+    # and on the GPU's sums: the square root halves the sums' relative error
+    imp = host(api.imatrix_importance(sums, counts))
+    assert _rel_close(imp, imp_o, 1e-5)
+
+
 def test_workload_iq2_xxs_256x512_end_to_end(api, orc):
     say("workload iq2_xxs_256x512")
     w, x, grid, spec = inputs.workload("iq2_xxs_256x512")
     sums, counts = api.imatrix_collect(dev(x), chunk_rows=1024)
-    imp = api.imatrix_importance(sums, counts)
-    s_o, c_o, _ = orc.collect(x)
-    assert _rel_close(host(sums)[0], s_o[0]) and int(host(counts)[0]) == 512
-    imp_h = host(imp)
-    want_imp, _ = orc.importance(host(sums), host(counts))
-    assert np.array_equal(imp_h, want_imp)
-    got = host(api.quantize("IQ2_XXS", dev(w), dev(grid), imp))
-    want, _ = orc.quantize("IQ2_XXS", w, grid, imp_h)
+    s_o, c_o, imp_o = _oracle_importance(orc, x)
+    assert int(c_o[0]) == 512
+    _check_statistics(api, orc, sums, counts, s_o, c_o, imp_o)
+    got = host(api.quantize("IQ2_XXS", dev(w), dev(grid), dev(imp_o)))
+    want, _ = orc.quantize("IQ2_XXS", w, grid, imp_o)
     assert np.array_equal(got, want)
 
 
@@ -454,8 +494,9 @@ def test_workload_full_size(api, orc, name):
     w, x, grid, spec = inputs.workload(name)
     fmt = spec["fmt"]
     sums, counts = api.imatrix_collect(dev_w(x, "bf16"), chunk_rows=1024)
-    imp = api.imatrix_importance(sums, counts)
-    imp_h = host(imp)
+    s_o, c_o, imp_h = _oracle_importance(orc, x)
+    _check_statistics(api, orc, sums, counts, s_o, c_o, imp_h)
+    imp = dev(imp_h)
     wd = dev_w(w, "bf16")
     got = host(api.quantize(fmt, wd, dev(grid), imp))
     if fmt.startswith("IQ1"):  # sampled rows (the oracle's IQ1 search is ~10x the IQ2 cost)
@@ -480,10 +521,11 @@ def test_workload_iq1_17408x5120_sampled_rows(api, orc, fmt):
     say("workload 17408x5120", fmt)
     w, x, grid, spec = inputs.workload("iq1_s_17408x5120")
     sums, counts = api.imatrix_collect(dev_w(x, "bf16"), chunk_rows=1024)
-    imp = api.imatrix_importance(sums, counts)
-    got = host(api.quantize(fmt, dev_w(w, "bf16"), dev(grid), imp))
+    s_o, c_o, imp_h = _oracle_importance(orc, x)
+    _check_statistics(api, orc, sums, counts, s_o, c_o, imp_h)
+    got = host(api.quantize(fmt, dev_w(w, "bf16"), dev(grid), dev(imp_h)))
     rid = np.sort(inputs.rng(1850).choice(w.shape[0], 16, replace=False))
-    want, _ = orc.quantize(fmt, w, grid, host(imp), row_ids=rid, threads=16)
+    want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid, threads=16)
     assert np.array_equal(got[rid], want)
 
 
@@ -494,15 +536,12 @@ def test_workload_moe_experts(api, orc):
     w, x, ids, grid, spec = inputs.moe_workload()
     E, rpe = spec["experts"], spec["rows_per_expert"]
     sums, counts = api.imatrix_collect(dev_w(x, "bf16"), dev(ids), E, chunk_rows=1024)
-    s_o, c_o, _ = orc.collect(x, ids, E)
-    c = host(counts)
-    assert np.array_equal(c, c_o) and (c == 0).sum() >= 5
-    s = host(sums)
-    assert _rel_close(s[c > 0], s_o[c > 0])
-    imp = api.imatrix_importance(sums, counts)
-    imp_h = host(imp)
+    s_o, c, imp_h = _oracle_importance(orc, x, ids, E)
+    assert (c == 0).sum() >= 5
+    _check_statistics(api, orc, sums, counts, s_o, c, imp_h)
     assert np.all(imp_h[c == 0] == 1.0)
-    got = host(api.quantize("IQ2_XXS", dev_w(w, "bf16"), dev(grid), imp, rows_per_expert=rpe))
+    assert np.all(host(api.imatrix_importance(sums, counts))[c == 0] == 1.0)
+    got = host(api.quantize("IQ2_XXS", dev_w(w, "bf16"), dev(grid), dev(imp_h), rows_per_expert=rpe))
     idle = np.flatnonzero(c == 0)
     g = inputs.rng(1900)
     rid = np.sort(np.concatenate([g.choice(w.shape[0], 40, replace=False), idle[:2] * rpe + 5,
