@@ -882,6 +882,12 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   __shared__ float s_r[UV][64];      // its cross term
   __shared__ float s_x[UV][64];      // its weights
   __shared__ float s_f[NC][64];      // its candidates' scores
+  // the revisited unit's rows of the damped-free block H (UV x 256), staged
+  // one revisit ahead: each thread prefetches HV4 float4 into registers at the
+  // start of a revisit and stores them once the parts have been formed
+  constexpr int HROW = UV * 256, NT = 64 * U, HV4 = HROW / 4 / NT;
+  static_assert(HROW % (4 * NT) == 0, "whole float4 per thread");
+  __shared__ __attribute__((aligned(16))) float s_h[HROW];
   const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
   const int64_t tile = L % A.tiles_per_e;
   const int64_t q = L / A.tiles_per_e;
@@ -962,12 +968,23 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   for (int k = 0; k < NCW; ++k)
 #pragma unroll
     for (int u = 0; u < U; ++u) qk[k][u] = v + U * k < NC ? s_buf[(u * NC + v + U * k) * 64 + lane] : 0.0f;
+  float4 hpre[HV4];
+#pragma unroll
+  for (int t = 0; t < HV4; ++t) hpre[t] = reinterpret_cast<const float4 *>(H)[threadIdx.x + t * NT];
+#pragma unroll
+  for (int t = 0; t < HV4; ++t) reinterpret_cast<float4 *>(s_h)[threadIdx.x + t * NT] = hpre[t];
   __syncthreads();
   // two passes over the units in ascending order
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll 1
     for (int u = 0; u < U; ++u) {
+      const bool more = pass == 0 || u + 1 < U;  // a next revisit exists
+      if (more) {
+        const float4 *src = reinterpret_cast<const float4 *>(H + ((u + 1) % U) * HROW);
+#pragma unroll
+        for (int t = 0; t < HV4; ++t) hpre[t] = src[threadIdx.x + t * NT];
+      }
       // the fields of this wave's share of unit u's choices do not depend on
       // the picks: their loads are issued before the parts are formed
       uint32_t rc[NCW][GPU];
@@ -979,7 +996,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
       if (v != u) {
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
-          const float *Hi = H + (u * UV + i) * 256 + v * UV;
+          const float *Hi = s_h + i * 256 + v * UV;
           float part = 0.0f;
 #pragma unroll
           for (int j = 0; j < UV; ++j) part = __builtin_fmaf(Hi[j], dwv[j], part);
@@ -990,6 +1007,10 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
         for (int i = 0; i < UV; ++i) s_x[i][lane] = xv[i];
       }
       __syncthreads();
+      if (more) {  // every wave has formed its part: the next revisit's rows replace these
+#pragma unroll
+        for (int t = 0; t < HV4; ++t) reinterpret_cast<float4 *>(s_h)[threadIdx.x + t * NT] = hpre[t];
+      }
       // cross term rows i = v, v + U, ...: the parts added in unit order
 #pragma unroll
       for (int t = 0; t < NI; ++t) {
@@ -1002,6 +1023,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
         }
       }
       __syncthreads();
+      float dwc[NCW][UV];
 #pragma unroll
       for (int k = 0; k < NCW; ++k) {
         const int c = v + U * k;
@@ -1015,27 +1037,34 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
             float y[8];
             record_values<F>(d, rc[k][gi], A.grid, y);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              dot = __builtin_fmaf(s_x[gi * 8 + j][lane] - y[j], s_r[gi * 8 + j][lane], dot);
+            for (int j = 0; j < 8; ++j) {
+              dwc[k][gi * 8 + j] = s_x[gi * 8 + j][lane] - y[j];
+              dot = __builtin_fmaf(dwc[k][gi * 8 + j], s_r[gi * 8 + j][lane], dot);
+            }
           }
           s_f[c][lane] = __builtin_fmaf(2.0f, dot, qu);
         }
       }
       __syncthreads();
+      // every wave finds each row's pick; the wave that scored it hands its
+      // residual to wave u through s_r (free until the next cross term)
+      float best = s_f[0][lane];
+      int pk = 0;
+      for (int c = 1; c < NC; ++c) {
+        const float f = s_f[c][lane];
+        if (f < best) { best = f; pk = c; }
+      }
+#pragma unroll
+      for (int k = 0; k < NCW; ++k)
+        if (pk == v + U * k) {
+#pragma unroll
+          for (int j = 0; j < UV; ++j) s_r[j][lane] = dwc[k][j];
+        }
+      __syncthreads();
       if (v == u) {
-        float best = s_f[0][lane];
-        pick = 0;
-        for (int c = 1; c < NC; ++c) {
-          const float f = s_f[c][lane];
-          if (f < best) { best = f; pick = c; }
-        }
+        pick = pk;
 #pragma unroll
-        for (int gi = 0; gi < GPU; ++gi) {
-          float y[8];
-          record_values<F>(d, rrow[pick * cstride + (v * GPU + gi) * rstride], A.grid, y);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) dwv[gi * 8 + j] = xv[gi * 8 + j] - y[j];
-        }
+        for (int j = 0; j < UV; ++j) dwv[j] = s_r[j][lane];
       }
     }
   }
