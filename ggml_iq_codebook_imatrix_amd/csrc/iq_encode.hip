@@ -905,7 +905,15 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   const uint32_t *rrow = rec + static_cast<int64_t>(b) * 32 * rstride + r;
   const int64_t cstride = A.nb * 32 * rstride;
 
-  // step A: every choice of unit v under its own damped block, CB at a time
+  // step A: every choice of unit v under its own damped block, CB at a time;
+  // the U diagonal sub-blocks H_vv ([v][i][j], U * UV * UV = HROW floats) are
+  // staged in s_h first
+  for (int t4 = threadIdx.x; t4 < HROW / 4; t4 += NT) {
+    const int vv = t4 / (UV * UV / 4), rem = t4 % (UV * UV / 4);
+    const int i = rem / (UV / 4), j4 = rem % (UV / 4);
+    reinterpret_cast<float4 *>(s_h)[t4] =
+        *reinterpret_cast<const float4 *>(H + static_cast<int64_t>(vv * UV + i) * 256 + vv * UV + 4 * j4);
+  }
   float xv[UV], dwv[UV];
   unit_weights<F>(A, r, b, v, xv);
   const float d = f16_bits_to_f32(dblk[r * A.nb + b]);
@@ -925,16 +933,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
           for (int j = 0; j < 8; ++j) dw[k][gi * 8 + j] = xv[gi * 8 + j] - y[j];
         }
       }
-      // H_vv is streamed on every batch: kept live across batches it would
-      // not fit the scalar registers
-      const float *Hv = H;
-      asm volatile("" : "+s"(Hv));
+      if (c0 == 0) __syncthreads();  // s_h holds every H_vv
       float err[CB];
 #pragma unroll
       for (int k = 0; k < CB; ++k) err[k] = 0.0f;
 #pragma unroll
       for (int i = 0; i < UV; ++i) {
-        const float *Hi = Hv + (v * UV + i) * 256 + v * UV;
+        const float *Hi = s_h + (v * UV + i) * UV;
         float y[CB];
 #pragma unroll
         for (int k = 0; k < CB; ++k) y[k] = 0.0f;
