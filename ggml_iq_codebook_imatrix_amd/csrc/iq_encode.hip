@@ -274,11 +274,11 @@ __device__ __forceinline__ float to_vgpr(float s) {
 // the least reduced error -- the same fp32 values the sweep compared -- and
 // its sign mask (IQ2) or shift bit (IQ1).
 // ---------------------------------------------------------------------------
-template <int F>
+template <int F, int CH>
 __device__ __forceinline__ void rescan_chunk(const float *__restrict__ grid, const float *gt, const GroupState<F> &S,
                                              int chs, float ssel, int hsel, int &kb, uint32_t &mfield) {
   using G = Geo<F>;
-  constexpr int CH = 32, N = G::N;
+  constexpr int N = G::N;
   const float dsel = hsel ? -0.125f : 0.125f;
   float bt = __builtin_inff();
   kb = chs * CH;
@@ -310,18 +310,18 @@ __device__ __forceinline__ void rescan_chunk(const float *__restrict__ grid, con
 }
 
 // IQ2 layouts rescan from a copy of the grid in LDS: chunk c's entry i sits at
-// float (32 c + i) * 8 + 4 c, so lanes rescanning different chunks read
+// float (CH c + i) * 8 + 4 c, so lanes rescanning different chunks read
 // different banks.  The weighted norm G_k is recomputed in the lane with the
 // same fmaf chain that built the table the sweep read, so it is the same value.
-__device__ __forceinline__ int lds_entry(int k) { return k * 8 + (k >> 5) * 4; }
+template <int CH>
+__device__ __forceinline__ int lds_entry(int k) { return k * 8 + (k / CH) * 4; }
 
-template <int F>
+template <int F, int CH>
 __device__ __forceinline__ void rescan_chunk_lds(const float *s_grid, const float a[8], const GroupState<F> &S,
                                                  int chs, float ssel, int &kb, uint32_t &mfield) {
-  constexpr int CH = 32;
   float bt = __builtin_inff();
   kb = chs * CH;
-  const float *base = s_grid + lds_entry(chs * CH);
+  const float *base = s_grid + lds_entry<CH>(chs * CH);
 #pragma unroll 4
   for (int i = 0; i < CH; ++i) {
     float g[8];
@@ -335,7 +335,7 @@ __device__ __forceinline__ void rescan_chunk_lds(const float *s_grid, const floa
   uint32_t mask = S.neg;
   if (S.odd) {
     float g[8];
-    load_entry(s_grid + lds_entry(kb), g);
+    load_entry(s_grid + lds_entry<CH>(kb), g);
     mask ^= 1u << S.flip_index(g);
   }
   mfield = mask;
@@ -413,11 +413,11 @@ __device__ __forceinline__ void pack_bytes(uint8_t *blk, int sb, int lane, const
 }
 
 // Copy the grid into LDS in the rescan layout (whole workgroup; ends with a barrier).
-template <int N>
+template <int N, int CH>
 __device__ __forceinline__ void stage_grid(const float *__restrict__ grid, float *s_grid) {
   for (int i = threadIdx.x; i < N * 2; i += blockDim.x) {
     const int k = i >> 1;
-    *reinterpret_cast<float4 *>(s_grid + lds_entry(k) + (i & 1) * 4) = reinterpret_cast<const float4 *>(grid)[i];
+    *reinterpret_cast<float4 *>(s_grid + lds_entry<CH>(k) + (i & 1) * 4) = reinterpret_cast<const float4 *>(grid)[i];
   }
   __syncthreads();
 }
@@ -436,7 +436,11 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   using G = Geo<F>;
   constexpr bool FIXED = MODE == FIXED_CHOICES;
   constexpr int WGG = G::WGG, GPU = G::GPU, N = G::N;
-  constexpr int CH = 32, NCH = N / CH;
+  // chunk of the first-minimum tracking: the every-choice sweeps rescan 16
+  // times per lane, so they keep shorter chunks (more bookkeeping, shorter rescans)
+  // (IQ1_M excepted: its every-choice sweep then needs more registers than
+  // four waves per SIMD allow)
+  constexpr int CH = ((MODE == EVERY || MODE == RECORDS) && F != IQ1_M) ? 8 : 32, NCH = N / CH;
   constexpr int UPW = WGG / GPU;                 // choice units per workgroup
   constexpr int SBS = 32 / WGG;                  // workgroups per block column
   // slots swept per lane: IQ2 16 choices; IQ1 8 scales x 2 shifts;
@@ -448,7 +452,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   // rescans read
   constexpr bool LDS_RESCAN = !G::IQ1 && (MODE == EVERY || MODE == RECORDS);
   constexpr int BEST_F = MODE == SEARCH ? WGG * NSLOT * 64 : 1;
-  constexpr int GRID_F = LDS_RESCAN ? N * 8 + (N / 32) * 4 : 1;
+  constexpr int GRID_F = LDS_RESCAN ? N * 8 + (N / CH) * 4 : 1;
   __shared__ __attribute__((aligned(16))) float s_u[BEST_F > GRID_F ? BEST_F : GRID_F];
   float (*s_best)[NSLOT][64] = reinterpret_cast<float (*)[NSLOT][64]>(s_u);
   __shared__ uint16_t s_k[WGG][64];
@@ -575,7 +579,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   }
 
   // ---- every choice: one field record per choice and group ----------------
-  if (LDS_RESCAN) stage_grid<N>(A.grid, s_u);
+  if (LDS_RESCAN) stage_grid<N, CH>(A.grid, s_u);
   if (MODE == RECORDS) {
     uint32_t *rp = A.rec + (static_cast<int64_t>(b) * 32 + gi) * A.rows + r;
     const int64_t cstride = static_cast<int64_t>(A.nb) * 32 * A.rows;
@@ -588,8 +592,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (LDS_RESCAN) rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
-      else rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F, CH>(s_u, a, S, chs, ssel, kb, mfield);
+      else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
       GroupFields f;
       f.d16 = d16;
       f.k = static_cast<uint32_t>(kb);
@@ -613,8 +617,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (LDS_RESCAN) rescan_chunk_lds<F>(s_u, a, S, chs, ssel, kb, mfield);
-      else rescan_chunk<F>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F, CH>(s_u, a, S, chs, ssel, kb, mfield);
+      else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
       int cu = c;
       if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
       __syncthreads();  // the previous choice's bytes have been read from LDS
@@ -697,7 +701,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
   }
   int kb;
   uint32_t mfield;
-  rescan_chunk<F>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
+  rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
   if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
 
   // ---- pack ----------------------------------------------------------------
