@@ -63,9 +63,9 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total) {
 // flags[e * nb + b] = 1 when the block's 256 importance values hold a
 // non-finite or negative value.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) impcheck_kernel(const float *__restrict__ imp, int64_t n,
-                                                        uint8_t *__restrict__ flags) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // (e * nb + b)
+__device__ __forceinline__ void impcheck_block(int64_t blk, const float *__restrict__ imp, int64_t n,
+                                               uint8_t *__restrict__ flags) {
+  const int64_t i = blk * 4 + (threadIdx.x >> 6);  // (e * nb + b)
   const int lane = threadIdx.x & 63;
   if (i >= n) return;
   const float4 q = reinterpret_cast<const float4 *>(imp + i * 256)[lane];  // cols = nb * 256
@@ -164,17 +164,16 @@ __device__ __forceinline__ void load_entry(const float *p, float g[8]) {
 }
 
 template <int F>
-__global__ void __launch_bounds__(256) gterm_kernel(const float *__restrict__ grid,
-                                                     const float *__restrict__ imp, int64_t cols,
-                                                     int64_t ntab, float *__restrict__ gtab) {
+__device__ __forceinline__ void gterm_block(int64_t blk, const float *__restrict__ grid,
+                                            const float *__restrict__ imp, int64_t ntab, float *__restrict__ gtab) {
   using G = Geo<F>;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t i = blk * 256 + threadIdx.x;
   if (i >= ntab * G::N) return;
   const int k = static_cast<int>(i % G::N);
   // N is a multiple of the block size, so a block lies in one table: the
   // importance values are wave-uniform
   static_assert(G::N % 256 == 0, "a 256-thread block covers entries of one table");
-  const int64_t tab = static_cast<int64_t>(blockIdx.x) * blockDim.x / G::N;  // = e * (cols / 8) + cg
+  const int64_t tab = blk * 256 / G::N;  // = e * (cols / 8) + cg
   float a[8], g[8];
   load_entry(grid + static_cast<int64_t>(k) * 8, g);
 #pragma unroll
@@ -197,6 +196,17 @@ __global__ void __launch_bounds__(256) gterm_kernel(const float *__restrict__ gr
       gtab[(tab * 2 + h) * G::N + k] = s;
     }
   }
+}
+
+// One launch for the two preparation passes: blocks [0, gblocks) build the
+// weighted-norm tables, the rest check the importance blocks.
+template <int F>
+__global__ void __launch_bounds__(256) prep_kernel(const float *__restrict__ grid, const float *__restrict__ imp,
+                                                   int64_t ntab, float *__restrict__ gtab, int64_t gblocks,
+                                                   int64_t nflags, uint8_t *__restrict__ flags) {
+  const int64_t blk = blockIdx.x;
+  if (blk < gblocks) gterm_block<F>(blk, grid, imp, ntab, gtab);
+  else impcheck_block(blk - gblocks, imp, nflags, flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -1104,14 +1114,10 @@ static int launch_quantize_t(EncArgs A, int mode, hipStream_t stream) {
   A.gtab_e_stride = A.imp ? cgs * NG * G::N : 0;
   A.gtab_cg_stride = A.imp ? NG * G::N : 0;
 
-  const int64_t gthreads = ntab * G::N;
-  hipLaunchKernelGGL(gterm_kernel<F>, dim3(static_cast<unsigned>((gthreads + 255) / 256)), dim3(256), 0, stream,
-                     A.grid, A.imp, A.cols, ntab, A.gtab);
-  if (impflags) {
-    const int64_t nf = A.E * A.nb;
-    hipLaunchKernelGGL(impcheck_kernel, dim3(static_cast<unsigned>((nf + 3) / 4)), dim3(256), 0, stream, A.imp, nf,
-                       impflags);
-  }
+  const int64_t gblocks = (ntab * G::N + 255) / 256;
+  const int64_t nf = impflags ? A.E * A.nb : 0;
+  hipLaunchKernelGGL(prep_kernel<F>, dim3(static_cast<unsigned>(gblocks + (nf + 3) / 4)), dim3(256), 0, stream,
+                     A.grid, A.imp, ntab, A.gtab, gblocks, nf, impflags);
   hipLaunchKernelGGL(anchor_kernel<F>, dim3(static_cast<unsigned>((nblocks + 7) / 8)), dim3(256), 0, stream, A,
                      static_cast<const uint8_t *>(impflags));
   A.tiles_per_e = (A.rpe + 63) / 64;
