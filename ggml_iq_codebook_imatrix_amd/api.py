@@ -192,7 +192,7 @@ def quantize(fmt, w: torch.Tensor, grid: torch.Tensor, importance: torch.Tensor 
     info = format_info(f)
     if tuple(grid.shape) != (info["grid_size"], 8):
         raise IQError(f"grid must be [{info['grid_size']}, 8]")
-    rpe = rows if rows_per_expert is None else int(rows_per_expert)
+    rpe = (rows or 1) if rows_per_expert is None else int(rows_per_expert)
     if importance is not None and (rpe < 1 or importance.dim() != 2 or importance.shape[1] != cols
                                    or importance.shape[0] * rpe != rows):
         raise IQError("importance must be [rows / rows_per_expert, cols]")
@@ -229,7 +229,7 @@ def quantize_every_choice(fmt, w: torch.Tensor, grid: torch.Tensor, importance: 
     info = format_info(f)
     if tuple(grid.shape) != (info["grid_size"], 8):
         raise IQError(f"grid must be [{info['grid_size']}, 8]")
-    rpe = rows if rows_per_expert is None else int(rows_per_expert)
+    rpe = (rows or 1) if rows_per_expert is None else int(rows_per_expert)
     if importance is not None and (rpe < 1 or importance.dim() != 2 or importance.shape[1] != cols
                                    or importance.shape[0] * rpe != rows):
         raise IQError("importance must be [rows / rows_per_expert, cols]")
@@ -258,7 +258,7 @@ def choice_search(fmt, w: torch.Tensor, grid: torch.Tensor, hess: torch.Tensor,
         raise IQError("w must be [rows, cols]")
     rows, cols = w.shape
     info = format_info(f)
-    rpe = rows if rows_per_expert is None else int(rows_per_expert)
+    rpe = (rows or 1) if rows_per_expert is None else int(rows_per_expert)
     if tuple(grid.shape) != (info["grid_size"], 8):
         raise IQError(f"grid must be [{info['grid_size']}, 8]")
     if rpe < 1 or rows % rpe or tuple(hess.shape) != (rows // rpe, cols // 256, 256, 256):

@@ -53,10 +53,10 @@ int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int
                        int num_experts, int chunk_rows, float *sums, int64_t *counts, int32_t *status,
                        hipStream_t stream) {
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!x || !sums || !counts) return IQ_ERR_NULL;
+  if (!sums || !counts || (T != 0 && !x)) return IQ_ERR_NULL;
   if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1) return IQ_ERR_ARG;
   if (ids && top_k < 1) return IQ_ERR_ARG;
-  if (!ids && num_experts != 1) return IQ_ERR_ARG;
+  if (!ids && num_experts != 1 && T != 0) return IQ_ERR_ARG;  // no tokens: ids may be NULL
   if (static_cast<int64_t>(num_experts) * K > (int64_t(1) << 40)) return IQ_ERR_ARG;
   return iq::launch_collect(x, dtype, T, K, ids, ids ? top_k : 0, num_experts, chunk_rows, sums, counts, status,
                             stream) == 0
@@ -67,10 +67,10 @@ int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int
 int iq_hessian_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
                        int num_experts, int chunk_rows, float *hess, int32_t *status, hipStream_t stream) {
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!x || !hess) return IQ_ERR_NULL;
+  if (!hess || (T != 0 && !x)) return IQ_ERR_NULL;
   if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1) return IQ_ERR_ARG;
   if (ids && top_k < 1) return IQ_ERR_ARG;
-  if (!ids && num_experts != 1) return IQ_ERR_ARG;
+  if (!ids && num_experts != 1 && T != 0) return IQ_ERR_ARG;  // no tokens: ids may be NULL
   if (K % 256 != 0) return IQ_ERR_SHAPE;
   if (static_cast<int64_t>(num_experts) * K > (int64_t(1) << 30) || T > (int64_t(1) << 31) - 1) return IQ_ERR_ARG;
   return iq::launch_hessian(x, dtype, T, K, ids, ids ? top_k : 0, num_experts, chunk_rows, hess, status, stream) == 0
@@ -92,7 +92,7 @@ static int quantize_common(int fmt, const void *w, int dtype, int64_t rows, int6
                            int32_t *status, bool every, hipStream_t stream) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!w || !grid || !out) return IQ_ERR_NULL;
+  if (!grid || (rows != 0 && (!w || !out))) return IQ_ERR_NULL;
   if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
   if (rows_per_expert < 1 || rows % rows_per_expert != 0) return IQ_ERR_SHAPE;
   if (cols / 256 > (int64_t(1) << 24) || rows > (int64_t(1) << 40)) return IQ_ERR_SHAPE;
@@ -137,7 +137,7 @@ int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t co
                      uint8_t *choices, int32_t *status, hipStream_t stream) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!w || !grid || !hess || !choices) return IQ_ERR_NULL;
+  if (!grid || (rows != 0 && (!w || !hess || !choices))) return IQ_ERR_NULL;
   if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
   if (rows_per_expert < 1 || rows % rows_per_expert != 0) return IQ_ERR_SHAPE;
   if (cols / 256 > (int64_t(1) << 24) || rows > (int64_t(1) << 40)) return IQ_ERR_SHAPE;
@@ -163,7 +163,7 @@ int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, co
                   int dtype, hipStream_t stream) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!packed || !grid || !out) return IQ_ERR_NULL;
+  if (!grid || (rows != 0 && (!packed || !out))) return IQ_ERR_NULL;
   if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
   if (rows * (cols / 256) * 32 / 256 >= (int64_t(1) << 31)) return IQ_ERR_SHAPE;
   return iq::launch_decode(fmt, packed, rows, cols, grid, out, dtype, stream) == 0 ? IQ_OK : IQ_ERR_HIP;

@@ -55,7 +55,9 @@ typedef enum { IQ_DTYPE_F32 = 0, IQ_DTYPE_BF16 = 1 } iq_dtype;
 #define IQ_OK 0
 #define IQ_ERR_FMT (-1)    /* unknown format                                  */
 #define IQ_ERR_DTYPE (-2)  /* unknown dtype                                   */
-#define IQ_ERR_NULL (-3)   /* a required pointer is NULL                      */
+#define IQ_ERR_NULL (-3)   /* a required pointer is NULL (data pointers of an
+                              empty input -- rows == 0 or T == 0 -- may be NULL;
+                              the call then enqueues nothing and returns IQ_OK) */
 #define IQ_ERR_SHAPE (-4)  /* cols % 256 != 0, rows % rows_per_expert != 0, ... */
 #define IQ_ERR_ARG (-5)    /* other invalid argument (top_k, chunk_rows, ...)   */
 #define IQ_ERR_HIP (-6)    /* HIP allocation or launch failure                */

@@ -234,6 +234,35 @@ def test_choice_search_full_size_sampled(api, orc, fmt):
     assert bad.size == 0, f"{len(bad)} picks differ, first {bad[:5].tolist()}"
 
 
+def test_empty_inputs(api):
+    """Zero rows or tokens: every entry point returns without launching and
+    leaves the outputs as they were."""
+    say("empty inputs")
+    w = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    for fmt in FORMATS:
+        info = api.format_info(fmt)
+        grid = dev(inputs.grid_for(fmt, GRID_SEED[fmt]))
+        p = api.quantize(fmt, w, grid, check=True)
+        assert tuple(p.shape) == (0, 2, info["block_bytes"])
+        ev = api.quantize_every_choice(fmt, w, grid)
+        assert tuple(ev.shape) == (info["num_choices"], 0, 2, info["block_bytes"])
+        hess = torch.zeros((0, 2, 256, 256), dtype=torch.float32, device="cuda")
+        ch = api.choice_search(fmt, w, grid, hess)
+        assert tuple(ch.shape) == (0, 2, info["choice_groups"])
+        y = api.dequantize(fmt, p, grid)
+        assert tuple(y.shape) == (0, 512)
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    sums = torch.full((1, 512), 3.0, device="cuda")
+    counts = torch.full((1,), 7, dtype=torch.int64, device="cuda")
+    api.imatrix_collect(x, sums=sums, counts=counts)
+    assert torch.all(sums == 3.0).item() and int(counts.item()) == 7
+    ids = torch.empty((0, 4), dtype=torch.int32, device="cuda")
+    s4, c4 = api.imatrix_collect(x, ids, 6)
+    assert not s4.any().item() and not c4.any().item()
+    h = api.hessian_collect(x)
+    assert not h.any().item()
+
+
 def test_encode_is_deterministic(api):
     say("determinism")
     fmt = "IQ2_S"
