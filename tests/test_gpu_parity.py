@@ -536,6 +536,14 @@ def test_workload_full_size(api, orc, name):
     want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid, threads=16)
     bad = np.argwhere((got[rid] != want).any(axis=2))
     assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
+    # decoded importance-weighted error: the GPU's decode of its payload against
+    # the oracle's decode of its own, within 1e-6 relative
+    y_g = host(api.dequantize(fmt, dev(got), dev(grid)))[rid].astype(np.float64)
+    a = imp_h[0].astype(np.float64)
+    wr = w[rid].astype(np.float64)
+    wmse_g = float((a * (wr - y_g) ** 2).sum() / (a * wr * wr).sum())
+    wmse_o = orc.weighted_mse(w[rid], orc.dequantize(fmt, want, len(rid), w.shape[1], grid), imp_h[0])
+    assert abs(wmse_g - wmse_o) <= 1e-6 * wmse_o
     if fmt == "IQ2_S":
         geo = orc.geometry(fmt)
         ch = np.full((w.shape[0], w.shape[1] // 256, geo["units"]), 7, np.uint8)
