@@ -214,6 +214,19 @@ def test_choice_search_parity(api, orc, fmt):
     assert np.array_equal(p, pw)
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_choice_search_f32_flat(api, orc, fmt):
+    """fp32 weights, flat importance, a ragged 64-row tile, one block column."""
+    say("choice search f32 flat", fmt)
+    grid = inputs.grid_for(fmt, GRID_SEED[fmt])
+    rows, cols = 77, 256
+    w = inputs.weight(rows, cols, 2500, 2501, bf16=False)
+    hess = _correlated_hessian(1, 1, 200, 2502)
+    got = host(api.choice_search(fmt, dev(w), dev(grid), dev(hess)))
+    want, _ = orc.choice_search(fmt, w, grid, hess)
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("fmt", ["IQ2_XS", "IQ1_M"])
 def test_choice_search_full_size_sampled(api, orc, fmt):
     """5632x2048 bf16 in the launch configuration bench.py times, with the
