@@ -291,9 +291,16 @@ def main() -> int:
         p_o, _ = oracle.quantize(fmt, w32[:n], grid32, imp_o, threads=threads)
         oracle.dequantize(fmt, p_o, n, cols, grid32)
         dt = time.perf_counter() - t
+        # the encode on one host thread, on the first 64 rows (same importance)
+        t1 = time.perf_counter()
+        oracle.quantize(fmt, w32[:64], grid32, imp_o, threads=1)
+        dt1 = time.perf_counter() - t1
         cpu = {"value": round(n * cols / dt / 1e6, 4), "unit": "M elem/s", "cores": threads, "kind": "oracle",
                "sample": f"whole step (collect 4096x2048, importance, IQ2_XS encode + decode) on the first {n} of "
-                         f"{rows} rows; {dt:.1f} s"}
+                         f"{rows} rows; {dt:.1f} s",
+               "encode_one_thread": {"value": round(64 * cols / dt1 / 1e6, 4), "unit": "M elem/s",
+                                     "sample": f"IQ2_XS encode of the first 64 rows on 1 thread; {dt1:.2f} s"},
+               "host_cpus": os.cpu_count()}
         log("cpu baseline", cpu)
 
     line = {
