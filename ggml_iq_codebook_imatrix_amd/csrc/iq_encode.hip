@@ -32,14 +32,16 @@
 // gfx950 design.  One wave per 8-value group and 64 rows per wave: the grid
 // entry and the weighted norm G_k are then the same for all 64 lanes, so they
 // arrive as scalar loads and cost no LDS bandwidth; G_k is precomputed once per
-// (expert, column group) by gterm_kernel and copied to a VGPR per entry so the
-// candidate FMAs can co-issue across waves.  The
-// sweep keeps, per slot, a running minimum per 32-entry chunk (v_min3 pairs)
-// and the index of the chunk holding the first minimum; after the unit's
-// choice is known the chosen chunk is rescanned to recover the exact entry.
-// A workgroup holds the groups whose payload bytes nobody else writes (one
-// 32-value sub-block; IQ1_M: 64 values), exchanges per-slot minima through LDS
-// to score its choice units, and packs its bytes itself.
+// (expert, column group) by the preparation kernel and copied to a VGPR per
+// entry so the candidate FMAs can co-issue across waves.  The sweep keeps, per
+// slot, a running minimum per chunk of CH entries (v_min3 pairs; CH = 32, 16
+// for IQ2_XXS, 8 in the every-choice sweeps) and the index of the chunk
+// holding the first minimum; after the unit's choice is known the chosen chunk
+// is rescanned to recover the exact entry.  A workgroup holds the groups whose
+// payload bytes nobody else writes (one 32-value sub-block; IQ1_M: 64 values),
+// exchanges per-slot minima through LDS to score its choice units, and packs
+// its bytes itself.  The file ends with the local-Hessian choice search and
+// its damping pass.
 
 #include "iq_common.hpp"
 #include "iq_internal.hpp"
@@ -280,7 +282,7 @@ __device__ __forceinline__ float to_vgpr(float s) {
 
 
 // ---------------------------------------------------------------------------
-// Rescan one 32-entry chunk under one (scale, shift) slot: the first entry with
+// Rescan one CH-entry chunk under one (scale, shift) slot: the first entry with
 // the least reduced error -- the same fp32 values the sweep compared -- and
 // its sign mask (IQ2) or shift bit (IQ1).
 // ---------------------------------------------------------------------------
