@@ -274,7 +274,24 @@ def main() -> int:
         moe["idle_experts"] = int((c3 == 0).sum().item())
         extras["moe_128x768x2048_iq2_xxs"] = moe
         log("moe", moe)
-        del wmd, xmd
+        # local-Hessian path per routed expert: each expert's Hessian blocks from
+        # its own tokens, the choice search over all 128 experts in one launch
+        hm = torch.zeros((E, cols // 256, 256, 256), dtype=torch.float32, device=dev)
+
+        def hm_fn():
+            hm.zero_()
+            api.hessian_collect(xmd, idsd, E, hess=hm)
+
+        mlh = {"hessian_collect_ms": round(timed(hm_fn, 3), 4)}
+        chm = api.choice_search("IQ2_XXS", wmd, gmd, hm, impm, rows_per_expert=rpe)
+        mlh["choice_search_ms"] = round(timed(lambda: api.choice_search("IQ2_XXS", wmd, gmd, hm, impm,
+                                                                       rows_per_expert=rpe, out=chm), 2), 4)
+        enc = time_encode("IQ2_XXS", wmd, gmd, impm, rpe=rpe, choices=chm, reps=3)
+        mlh["fixed_encode_ms"] = enc["encode_ms"]
+        mlh["path_ms"] = round(mlh["hessian_collect_ms"] + mlh["choice_search_ms"] + enc["encode_ms"], 4)
+        extras["moe_local_hessian_iq2_xxs"] = mlh
+        log("moe local hessian", mlh)
+        del hm, chm, wmd, xmd
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------
     cpu = None

@@ -418,8 +418,8 @@ template <int DT>
 __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x, int64_t T, int64_t K,
                                                      const int32_t *__restrict__ ids, int top_k, int E,
                                                      int chunk_rows, int W, const uint32_t *__restrict__ bm,
-                                                     int64_t split_len, float *__restrict__ dst, bool accumulate,
-                                                     int32_t *status) {
+                                                     const uint8_t *__restrict__ dup, int64_t split_len,
+                                                     float *__restrict__ dst, bool accumulate, int32_t *status) {
   constexpr int RS = DT == 1 ? 40 : 33;  // LDS row: 32 tokens + padding (bf16 80 B, f32 132 B)
   using elem_t = typename std::conditional<DT == 1, uint16_t, float>::type;
   __shared__ __attribute__((aligned(16))) elem_t sA[64][RS];
@@ -449,72 +449,113 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // routed token stream, advanced by lane 0 only: the word being read (its
-  // remaining bits and the token of bit 0), the next token to read a word at,
-  // and the repeats still owed to the last token taken
+  // token stream.  Dense: the range in order.  Routed: advanced by lane 0 from
+  // the bitmap words (the word being read: its remaining bits, the token of
+  // bit 0 and, per token, whether it names an expert twice), repeating a token
+  // as often as e appears in its ids
   int64_t tw = t0, wbase = 0, last = 0;
-  uint32_t bits = 0u;
+  uint32_t bits = 0u, dbits = 0u;
   int pending = 0;
-  int64_t cur = t0;  // dense stream
+  int64_t cur = t0;
   bool finite = true;
-  while (true) {
+  // next batch of tokens into s_tok; returns how many (uniform)
+  auto fill = [&]() -> int {
     int nt = 0;
     if (ids == nullptr) {
       nt = static_cast<int>((t1 - cur < kHTok) ? t1 - cur : kHTok);
       if (lane < kHTok) s_tok[lane] = lane < nt ? static_cast<int>(cur + lane) : -1;
       cur += nt;
-    } else {
-      if (lane == 0) {
-        while (nt < kHTok) {
-          if (pending > 0) {
-            s_tok[nt++] = static_cast<int>(last);
-            --pending;
-            continue;
-          }
-          if (bits == 0u) {
-            if (tw >= t1) break;
-            const int64_t ch = tw / chunk_rows, p = tw - ch * chunk_rows;
-            const int sh = static_cast<int>(p & 31);
-            wbase = tw - sh;
-            bits = (bm[(ch * E + e) * W + (p >> 5)] >> sh) << sh;
-            int64_t next = ch * chunk_rows + (p | 31) + 1;
-            if (next > (ch + 1) * chunk_rows) next = (ch + 1) * chunk_rows;
-            if (next > t1) next = t1;
-            if (next - wbase < 32) bits &= (1u << (next - wbase)) - 1u;
-            tw = next;
-            continue;
-          }
-          last = wbase + __builtin_ctz(bits);
-          bits &= bits - 1u;
-          int mult = 0;
-          for (int s = 0; s < top_k; ++s) mult += ids[last * top_k + s] == e;
-          s_tok[nt++] = static_cast<int>(last);
-          pending = mult - 1;
-        }
-        for (int q = nt; q < kHTok; ++q) s_tok[q] = -1;
-      }
-      nt = __shfl(nt, 0);
+      return nt;
     }
-    __syncthreads();
-    if (nt == 0) break;
+    if (lane == 0) {
+      while (nt < kHTok) {
+        if (pending > 0) {
+          s_tok[nt++] = static_cast<int>(last);
+          --pending;
+          continue;
+        }
+        if (bits == 0u) {
+          if (tw >= t1) break;
+          const int64_t ch = tw / chunk_rows, p = tw - ch * chunk_rows;
+          const int sh = static_cast<int>(p & 31);
+          wbase = tw - sh;
+          bits = (bm[(ch * E + e) * W + (p >> 5)] >> sh) << sh;
+          int64_t next = ch * chunk_rows + (p | 31) + 1;
+          if (next > (ch + 1) * chunk_rows) next = (ch + 1) * chunk_rows;
+          if (next > t1) next = t1;
+          if (next - wbase < 32) bits &= (1u << (next - wbase)) - 1u;
+          tw = next;
+          // repeat flags of the word's member tokens, one bit each
+          dbits = 0u;
+          for (uint32_t mb = bits; mb; mb &= mb - 1u) {
+            const int z = __builtin_ctz(mb);
+            dbits |= (dup[wbase + z] ? 1u : 0u) << z;
+          }
+          continue;
+        }
+        const int bit = __builtin_ctz(bits);
+        last = wbase + bit;
+        bits &= bits - 1u;
+        int mult = 1;
+        if ((dbits >> bit) & 1u) {  // rare: count the repeats of e in this token's ids
+          mult = 0;
+          for (int s = 0; s < top_k; ++s) mult += ids[last * top_k + s] == e;
+        }
+        s_tok[nt++] = static_cast<int>(last);
+        pending = mult - 1;
+      }
+      for (int q = nt; q < kHTok; ++q) s_tok[q] = -1;
+    }
+    return __shfl(nt, 0);
+  };
+  // this lane's share of a batch: bf16 -- column pair cp of both tiles for token
+  // octets g = lane/32, lane/32 + 2; f32 -- 4 columns of one token, 8 times
+  constexpr int NLD = DT == 1 ? 16 : 32;
+  uint32_t ra[NLD], rb[NLD];
+  auto issue = [&]() {
     if (DT == 1) {
-      // lane: column pair cp (columns 2cp, 2cp+1 of the tile), token octets tg, tg + 2
       const int cp = lane & 31;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int g = (lane >> 5) + 2 * it;
-        uint32_t va[8], vb[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int tok = s_tok[8 * g + j];
-          va[j] = 0u;
-          vb[j] = 0u;
+          ra[it * 8 + j] = 0u;
+          rb[it * 8 + j] = 0u;
           if (tok >= 0) {
             const uint16_t *xr = static_cast<const uint16_t *>(x) + static_cast<int64_t>(tok) * K;
-            va[j] = *reinterpret_cast<const uint32_t *>(xr + colA + 2 * cp);
-            vb[j] = *reinterpret_cast<const uint32_t *>(xr + colB + 2 * cp);
+            ra[it * 8 + j] = *reinterpret_cast<const uint32_t *>(xr + colA + 2 * cp);
+            rb[it * 8 + j] = *reinterpret_cast<const uint32_t *>(xr + colB + 2 * cp);
           }
         }
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int qd = lane + 64 * it;
+        const int tt = qd >> 4, cc = (qd & 15) * 4;
+        const int tok = s_tok[tt];
+        float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tok >= 0) {
+          const float *xr = static_cast<const float *>(x) + static_cast<int64_t>(tok) * K;
+          va = *reinterpret_cast<const float4 *>(xr + colA + cc);
+          vb = *reinterpret_cast<const float4 *>(xr + colB + cc);
+        }
+        ra[4 * it] = __float_as_uint(va.x); ra[4 * it + 1] = __float_as_uint(va.y);
+        ra[4 * it + 2] = __float_as_uint(va.z); ra[4 * it + 3] = __float_as_uint(va.w);
+        rb[4 * it] = __float_as_uint(vb.x); rb[4 * it + 1] = __float_as_uint(vb.y);
+        rb[4 * it + 2] = __float_as_uint(vb.z); rb[4 * it + 3] = __float_as_uint(vb.w);
+      }
+    }
+  };
+  auto stage = [&]() {
+    if (DT == 1) {
+      const int cp = lane & 31;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int g = (lane >> 5) + 2 * it;
+        const uint32_t *va = ra + it * 8, *vb = rb + it * 8;
         uint4 a0, a1, b0, b1;
         uint32_t *pa0 = &a0.x, *pa1 = &a1.x, *pb0 = &b0.x, *pb1 = &b1.x;
 #pragma unroll
@@ -534,24 +575,32 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
         *reinterpret_cast<uint4 *>(&sB[2 * cp + 1][8 * g]) = b1;
       }
     } else {
-      // lane: 4 columns cc..cc+3 of one token per iteration
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int qd = lane + 64 * it;
         const int tt = qd >> 4, cc = (qd & 15) * 4;
-        const int tok = s_tok[tt];
-        float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tok >= 0) {
-          const float *xr = static_cast<const float *>(x) + static_cast<int64_t>(tok) * K;
-          va = *reinterpret_cast<const float4 *>(xr + colA + cc);
-          vb = *reinterpret_cast<const float4 *>(xr + colB + cc);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float av = __uint_as_float(ra[4 * it + c]);
+          sA[cc + c][tt] = av;
+          sB[cc + c][tt] = __uint_as_float(rb[4 * it + c]);
+          finite = finite && finite_f(av);
         }
-        sA[cc][tt] = va.x; sA[cc + 1][tt] = va.y; sA[cc + 2][tt] = va.z; sA[cc + 3][tt] = va.w;
-        sB[cc][tt] = vb.x; sB[cc + 1][tt] = vb.y; sB[cc + 2][tt] = vb.z; sB[cc + 3][tt] = vb.w;
-        finite = finite && finite_f(va.x) && finite_f(va.y) && finite_f(va.z) && finite_f(va.w);
       }
     }
+  };
+  int nt = fill();
+  __syncthreads();
+  if (nt > 0) {
+    issue();
+    stage();
+  }
+  __syncthreads();
+  while (nt > 0) {
+    // the next batch's tokens and loads are in flight while this one multiplies
+    const int nn = fill();
     __syncthreads();
+    if (nn > 0) issue();
     if (DT == 1) {
 #pragma unroll
       for (int ks = 0; ks < kHTok / 16; ++ks) {
@@ -584,6 +633,9 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
       }
     }
     __syncthreads();
+    if (nn > 0) stage();
+    __syncthreads();
+    nt = nn;
   }
   if (!finite) raise_status(status, ST_NONFINITE);
   // dst: hess itself (one split, accumulate) or this split's partial blocks
@@ -635,25 +687,28 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   nsplit = (T + split_len - 1) / split_len;
   const int64_t hn = static_cast<int64_t>(E) * (K / 256) * 65536;
   const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
+  const size_t dbytes = ids ? static_cast<size_t>(T) : 0;
   const size_t pbytes = nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0;
   void *scratch = nullptr;
-  const size_t off_b = (pbytes + 255) & ~size_t(255);
-  if (off_b + bbytes > 0 && hipMallocAsync(&scratch, off_b + bbytes + 256, stream) != hipSuccess) return -1;
+  const size_t off_b = (pbytes + 255) & ~size_t(255), off_d = off_b + ((bbytes + 255) & ~size_t(255));
+  if (off_d + dbytes > 0 && hipMallocAsync(&scratch, off_d + dbytes + 256, stream) != hipSuccess) return -1;
   float *partial = static_cast<float *>(scratch);
   uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + off_b) : nullptr;
+  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(static_cast<char *>(scratch) + off_d) : nullptr;
   if (ids)
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
-                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm,
-                       static_cast<uint8_t *>(nullptr), status);
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, dup, status);
   float *dst = nsplit > 1 ? partial : hess;
   const bool accumulate = nsplit == 1;
   const dim3 g(static_cast<unsigned>(ntiles * nsplit));
   if (dtype == 1)
     hipLaunchKernelGGL(hessian_kernel<1>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E, chunk_rows, W,
-                       static_cast<const uint32_t *>(bm), split_len, dst, accumulate, status);
+                       static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), split_len, dst,
+                       accumulate, status);
   else
     hipLaunchKernelGGL(hessian_kernel<0>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E, chunk_rows, W,
-                       static_cast<const uint32_t *>(bm), split_len, dst, accumulate, status);
+                       static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), split_len, dst,
+                       accumulate, status);
   if (nsplit > 1)
     hipLaunchKernelGGL(hessian_combine_kernel, dim3(static_cast<unsigned>((hn + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float *>(partial), nsplit, hn, hess);
