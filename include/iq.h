@@ -91,10 +91,11 @@ int iq_format_info(int fmt, iq_format_info_t *out);
  *
  *  x        (device) [T, K] activations, dtype f32 or bf16.
  *  ids      (device) [T, top_k] int32 routed expert ids, or NULL for a dense
- *           weight (then num_experts must be 1 and top_k is ignored).
- *  chunk_rows  rows reduced per chunk (1024 in [2735]); partial sums of each
- *           chunk are added to `sums` in chunk order, so results do not depend
- *           on the launch and repeat bit for bit.
+ *           weight (then num_experts must be 1 and top_k is ignored; with
+ *           T == 0 ids may be NULL for any num_experts).
+ *  chunk_rows  rows reduced per chunk (1024 in [2735]); each chunk is reduced
+ *           in fixed slices whose partial sums are added to `sums` in order,
+ *           so results do not depend on the launch and repeat bit for bit.
  *  sums     (device) [num_experts, K] f32, ACCUMULATED: sums[e][j] += sum over
  *           the (t, s) pairs with ids[t][s] == e of x[t][j]^2 (a duplicate id in
  *           one token counts per occurrence).
@@ -197,8 +198,9 @@ int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t co
  *  hess     (device) [num_experts, K/256, 256, 256] f32, ACCUMULATED:
  *           hess[e][b][i][j] += sum over the (t, s) pairs with ids[t][s] == e of
  *           x[t][256b + i] * x[t][256b + j] (dense: every token, e = 0).  Each
- *           block is exactly symmetric.  Tokens are added in ascending order in
- *           fixed token ranges, so results repeat bit for bit.
+ *           block is exactly symmetric.  Tokens are added in ascending order
+ *           (a token naming e twice, twice in a row) in fixed token ranges, so
+ *           results repeat bit for bit.
  *  status   (device, nullable): IQ_STATUS_NONFINITE when a token that reached an
  *           expert holds a non-finite value; IQ_STATUS_BADID as
  *           iq_imatrix_collect.
