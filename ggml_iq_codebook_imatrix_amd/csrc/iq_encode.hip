@@ -443,8 +443,15 @@ __device__ __forceinline__ void stage_grid(const float *__restrict__ grid, float
 // as one word per (choice, group, row) for the choice search.
 enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2, RECORDS = 3 };
 
+// Waves per SIMD the compiler must fit: IQ2_S and IQ1_S searches gain from a
+// fifth (measured), the others keep their register budget.
 template <int F, int MODE>
-__global__ void __launch_bounds__(64 * Geo<F>::WGG) search_kernel(EncArgs A) {
+constexpr int search_min_waves() {
+  return (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_S || F == IQ1_S) ? 5 : 1;
+}
+
+template <int F, int MODE>
+__global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>())) search_kernel(EncArgs A) {
   using G = Geo<F>;
   constexpr bool FIXED = MODE == FIXED_CHOICES;
   constexpr int WGG = G::WGG, GPU = G::GPU, N = G::N;
