@@ -243,12 +243,15 @@ struct GroupState {
     f4 = odd ? 4.0f : 0.0f;
   }
 
-  // IQ2: -2 P'_k for grid entry g;  IQ1: Q_k (before the shift term)
+  // IQ2: -2 P'_k for grid entry g;  IQ1: Q_k (before the shift term).  PAR
+  // false drops the parity term, which is exact for an even-parity group
+  // (f4 = 0: the term adds +0 to a sum that is never -0)
+  template <bool PAR = Geo<F>::PARITY>
   __device__ __forceinline__ float term(const float g[8]) const {
     float p = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) p = __builtin_fmaf(nax[j], g[j], p);
-    if (Geo<F>::PARITY) {
+    if (PAR) {
       float fm = ax[0] * g[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) fm = fminf(fm, ax[j] * g[j]);
@@ -447,7 +450,9 @@ enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2, RECORDS = 3 };
 // fifth (measured), the others keep their register budget.
 template <int F, int MODE>
 constexpr int search_min_waves() {
-  return (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_S || F == IQ1_S) ? 5 : 1;
+  return (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_S || F == IQ1_S) ? 5
+         : (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_XXS || F == IQ2_XS) ? 4
+                                                                                       : 1;
 }
 
 template <int F, int MODE>
@@ -479,6 +484,17 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   __shared__ uint16_t s_k[WGG][64];
   __shared__ uint8_t s_m[WGG][64];
   __shared__ uint8_t s_c[UPW][64];
+  // Parity-sorted items (IQ2_XXS/XS search and fixed encodes): the workgroup's
+  // WGG x 64 (group, row) items are dealt to the waves odd-parity first, so
+  // about one wave in three holds only even-parity groups and sweeps without
+  // the parity term.  A wave then mixes groups, so the weighted norms come from
+  // an LDS copy of the workgroup's tables instead of scalar loads.
+  constexpr bool SORTED = G::PARITY && (MODE == SEARCH || MODE == FIXED_CHOICES);
+  __shared__ uint16_t s_items[SORTED ? WGG * 64 : 1];
+  __shared__ int s_nodd[SORTED ? WGG : 1];
+  // row stride N + 2: the (up to WGG) groups a wave reads per entry pair sit in
+  // different banks
+  __shared__ __attribute__((aligned(8))) float s_g[SORTED ? WGG : 1][SORTED ? N + 2 : 1];
 
   const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
   const int64_t tile = L % A.tiles_per_e;
@@ -488,12 +504,48 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   const int b = colset / SBS, sb = colset % SBS;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t rin = tile * 64 + lane;
+  // the rows this wave packs (lane = row)
+  const bool valid_pack = tile * 64 + lane < A.rpe;
+  const int64_t r_pack = e * A.rpe + (valid_pack ? tile * 64 + lane : A.rpe - 1);
+  // this thread's item: group gw of the workgroup, row rl of the tile
+  int gw = wave, rl = lane;
+  bool all_even = false;  // wave-uniform
+  if (SORTED) {
+    float xn[8];
+    load8(A.w, A.dtype, r_pack * A.cols + (static_cast<int64_t>(b) * 32 + sb * WGG + wave) * 8, xn);
+    uint32_t neg = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) neg |= (xn[j] < 0.0f ? 1u : 0u) << j;
+    const bool odd = __builtin_popcount(neg) & 1;
+    const uint64_t bal = __ballot(odd);
+    if (lane == 0) s_nodd[wave] = __builtin_popcountll(bal);
+    for (int i = threadIdx.x; i < WGG * N; i += 64 * WGG) {
+      const int64_t cgw = static_cast<int64_t>(b) * 32 + sb * WGG + i / N;
+      s_g[i / N][i % N] = A.gtab[e * A.gtab_e_stride + cgw * A.gtab_cg_stride + i % N];
+    }
+    __syncthreads();
+    int n_odd = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < WGG; ++w) {
+      n_odd += s_nodd[w];
+      before += w < wave ? s_nodd[w] : 0;
+    }
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int pos = odd ? before + __builtin_popcountll(bal & below)
+                        : n_odd + (wave * 64 - before) + __builtin_popcountll(~bal & below);
+    s_items[pos] = static_cast<uint16_t>((wave << 6) | lane);
+    __syncthreads();
+    const int it = s_items[wave * 64 + lane];
+    gw = it >> 6;
+    rl = it & 63;
+    all_even = wave * 64 >= __builtin_amdgcn_readfirstlane(n_odd);
+  }
+  const int64_t rin = tile * 64 + rl;
   const bool valid = rin < A.rpe;
   const int64_t r = e * A.rpe + (valid ? rin : A.rpe - 1);
-  const int gi = sb * WGG + wave;                  // group within the block
+  const int gi = sb * WGG + gw;                    // group within the block
   const int64_t cg = static_cast<int64_t>(b) * 32 + gi;
-  const int uw = wave / GPU;                       // unit within the workgroup
+  const int uw = gw / GPU;                         // unit within the workgroup
   const int unit = gi / GPU;                       // unit within the block
 
   const uint16_t d16 = A.dscr[r * A.nb + b];
@@ -543,6 +595,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
 #pragma unroll
   for (int s = 0; s < NSLOT; ++s) { best[s] = __builtin_inff(); bidx[s] = 0; }
 
+  auto sweep = [&](auto par) {
+  constexpr bool PAR = decltype(par)::value;
   for (int ch = 0; ch < NCH; ++ch) {
     float cm[NSLOT];
 #pragma unroll
@@ -551,6 +605,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
     for (int i = 0; i < CH; i += 2) {
       const int k = ch * CH + i;
       float t0[NSLOT], t1[NSLOT];
+      float2 gk2 = make_float2(0.0f, 0.0f);
+      if (SORTED) gk2 = *reinterpret_cast<const float2 *>(&s_g[gw][k]);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         float *t = p ? t1 : t0;
@@ -558,9 +614,9 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
         float g[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) g[j] = gp[j];
-        const float q2 = S.term(g);
+        const float q2 = S.template term<PAR>(g);
         if (!G::IQ1) {
-          const float Gk = to_vgpr(gt[k + p]);
+          const float Gk = SORTED ? (p ? gk2.y : gk2.x) : to_vgpr(gt[k + p]);
           if (FIXED) {
             t[0] = __builtin_fmaf(fs, Gk, q2);
           } else {
@@ -597,6 +653,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
       best[s] = upd ? cm[s] : best[s];
       bidx[s] = upd ? ch : bidx[s];
     }
+  }
+  };
+  if constexpr (SORTED) {
+    if (all_even) sweep(std::integral_constant<bool, false>{});
+    else sweep(std::integral_constant<bool, true>{});
+  } else {
+    sweep(std::integral_constant<bool, G::PARITY>{});
   }
 
   // ---- every choice: one field record per choice and group ----------------
@@ -661,7 +724,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
     slot = (F == IQ1_M) ? (best[1] < best[0] ? 1 : 0) : 0;
   } else {
 #pragma unroll
-    for (int s = 0; s < NSLOT; ++s) s_best[wave][s][lane] = best[s];
+    for (int s = 0; s < NSLOT; ++s) s_best[gw][s][rl] = best[s];
     __syncthreads();
     float bs = 0.0f;
 #pragma unroll
@@ -672,14 +735,14 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
         const int w = uw * GPU + i;
         float bb, s;
         if (F == IQ1_M) {
-          const float b0 = s_best[w][c][lane], b1 = s_best[w][8 + c][lane];
+          const float b0 = s_best[w][c][rl], b1 = s_best[w][8 + c][rl];
           bb = (b1 < b0) ? b1 : b0;          // tie: the lower shift
           s = sc[c];
         } else if (F == IQ1_S) {
-          bb = s_best[w][c][lane];
+          bb = s_best[w][c][rl];
           s = sc[c & 7];
         } else {
-          bb = s_best[w][c][lane];
+          bb = s_best[w][c][rl];
           s = sc[c];
         }
         const float ev = s * bb;
@@ -722,16 +785,17 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   }
   int kb;
   uint32_t mfield;
-  rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, hsel, kb, mfield);
+  rescan_chunk<F, CH>(A.grid, SORTED ? &s_g[gw][0] : gt, S, chs, ssel, hsel, kb, mfield);
   if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
 
   // ---- pack ----------------------------------------------------------------
-  s_k[wave][lane] = static_cast<uint16_t>(kb);
-  s_m[wave][lane] = static_cast<uint8_t>(mfield);
-  if (wave % GPU == 0) s_c[uw][lane] = static_cast<uint8_t>(cu);
+  s_k[gw][rl] = static_cast<uint16_t>(kb);
+  s_m[gw][rl] = static_cast<uint8_t>(mfield);
+  if (gw % GPU == 0) s_c[uw][rl] = static_cast<uint8_t>(cu);
   __syncthreads();
-  if (wave != 0 || !valid) return;
-  pack_bytes<F>(A.out + (r * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, d16);
+  if (wave != 0 || !valid_pack) return;
+  const uint16_t d16p = SORTED ? A.dscr[r_pack * A.nb + b] : d16;
+  pack_bytes<F>(A.out + (r_pack * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, d16p);
 }
 
 // ---------------------------------------------------------------------------
