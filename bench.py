@@ -205,9 +205,10 @@ def main() -> int:
         extras["every_choice_5632x2048"] = ev
         log("every choice", ev)
 
-        # local-Hessian path: Hessian blocks from the same 4,096 tokens, the
-        # choice search (every-choice encode + unit picks + two passes), then
-        # the encode under the picked choices
+        # local-Hessian path: Hessian blocks from the same 4,096 tokens, then
+        # the choice search (every-choice encode + unit picks + two passes)
+        # writing the payload under its picks; for comparison, the choice
+        # search alone and a separate encode under the picked choices
         def timed(fn, reps):
             fn()
             torch.cuda.synchronize()
@@ -230,12 +231,14 @@ def main() -> int:
         lh["hessian_TFLOP_s"] = round(hess_flops / (lh["hessian_collect_ms"] * 1e-3) / 1e12, 2)
         for f in api.FORMATS:
             g = torch.from_numpy(inputs.grid_for(f, GRID_SEED[f])).to(dev)
-            chs = api.choice_search(f, w, g, hess, imp)
+            chs, pay = api.choice_search(f, w, g, hess, imp, payload=True)
             cs_ms = timed(lambda: api.choice_search(f, w, g, hess, imp, out=chs), max(2, args.reps // 3))
+            csp_ms = timed(lambda: api.choice_search(f, w, g, hess, imp, out=chs, payload=pay), max(2, args.reps // 3))
             enc = time_encode(f, w, g, imp, choices=chs)
-            lh[f] = {"choice_search_ms": round(cs_ms, 4), "fixed_encode_ms": enc["encode_ms"],
-                     "path_ms": round(lh["hessian_collect_ms"] + cs_ms + enc["encode_ms"], 4)}
-            del chs
+            lh[f] = {"choice_search_ms": round(cs_ms, 4), "with_payload_ms": round(csp_ms, 4),
+                     "separate_fixed_encode_ms": enc["encode_ms"],
+                     "path_ms": round(lh["hessian_collect_ms"] + csp_ms, 4)}
+            del chs, pay
         extras["local_hessian_5632x2048"] = lh
         log("local hessian", lh)
         del hess
@@ -283,15 +286,14 @@ def main() -> int:
             api.hessian_collect(xmd, idsd, E, hess=hm)
 
         mlh = {"hessian_collect_ms": round(timed(hm_fn, 3), 4)}
-        chm = api.choice_search("IQ2_XXS", wmd, gmd, hm, impm, rows_per_expert=rpe)
-        mlh["choice_search_ms"] = round(timed(lambda: api.choice_search("IQ2_XXS", wmd, gmd, hm, impm,
-                                                                       rows_per_expert=rpe, out=chm), 2), 4)
-        enc = time_encode("IQ2_XXS", wmd, gmd, impm, rpe=rpe, choices=chm, reps=3)
-        mlh["fixed_encode_ms"] = enc["encode_ms"]
-        mlh["path_ms"] = round(mlh["hessian_collect_ms"] + mlh["choice_search_ms"] + enc["encode_ms"], 4)
+        chm, paym = api.choice_search("IQ2_XXS", wmd, gmd, hm, impm, rows_per_expert=rpe, payload=True)
+        mlh["with_payload_ms"] = round(timed(lambda: api.choice_search("IQ2_XXS", wmd, gmd, hm, impm,
+                                                                      rows_per_expert=rpe, out=chm, payload=paym),
+                                             2), 4)
+        mlh["path_ms"] = round(mlh["hessian_collect_ms"] + mlh["with_payload_ms"], 4)
         extras["moe_local_hessian_iq2_xxs"] = mlh
         log("moe local hessian", mlh)
-        del hm, chm, wmd, xmd
+        del hm, chm, paym, wmd, xmd
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------
     cpu = None

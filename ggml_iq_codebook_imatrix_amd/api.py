@@ -32,7 +32,7 @@ SIGNATURES = {
     "iq_imatrix_importance": ([_P, _P, _I, _I64, _F, _P, _P, _P], _I),
     "iq_quantize": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
     "iq_quantize_every_choice": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P], _I),
-    "iq_choice_search": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _F, _P, _P, _P], _I),
+    "iq_choice_search": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _F, _P, _P, _P, _P], _I),
     "iq_dequantize": ([_I, _P, _I64, _I64, _P, _P, _I, _P], _I),
     "iq_time_next_search": ([_P, _P], _I),
     "iq_error_string": ([_I], ctypes.c_char_p),
@@ -250,9 +250,11 @@ def quantize_every_choice(fmt, w: torch.Tensor, grid: torch.Tensor, importance: 
 def choice_search(fmt, w: torch.Tensor, grid: torch.Tensor, hess: torch.Tensor,
                   importance: torch.Tensor | None = None, rows_per_expert: int | None = None,
                   perc_damp: float = 0.3, out: torch.Tensor | None = None,
-                  status: torch.Tensor | None = None) -> torch.Tensor:
+                  status: torch.Tensor | None = None, payload: torch.Tensor | bool | None = None):
     """Local-Hessian choice search -> uint8 choices [rows, cols/256, choice_groups];
-    hess: [rows / rows_per_expert, cols/256, 256, 256] f32 diagonal Hessian blocks."""
+    hess: [rows / rows_per_expert, cols/256, 256, 256] f32 diagonal Hessian blocks.
+    With `payload` (True, or a uint8 [rows, cols/256, block_bytes] tensor to fill)
+    the payload under the picks is written as well and (choices, payload) returned."""
     f = _fmt(fmt)
     if w.dim() != 2:
         raise IQError("w must be [rows, cols]")
@@ -270,12 +272,18 @@ def choice_search(fmt, w: torch.Tensor, grid: torch.Tensor, hess: torch.Tensor,
         out = torch.empty((rows, cols // 256, info["choice_groups"]), dtype=torch.uint8, device=w.device)
     if w.dtype not in DTYPE:
         raise IQError(f"unsupported dtype {w.dtype}")
+    if payload is True:
+        payload = torch.empty((rows, cols // 256, info["block_bytes"]), dtype=torch.uint8, device=w.device)
+    elif payload is False:
+        payload = None
+    if payload is not None and tuple(payload.shape) != (rows, cols // 256, info["block_bytes"]):
+        raise IQError(f"payload must be [rows, cols/256, {info['block_bytes']}]")
     rc = lib().iq_choice_search(f, _dev(w, "w"), DTYPE[w.dtype], rows, cols, rpe, _dev(grid, "grid", torch.float32),
                                 _dev(importance, "importance", torch.float32), _dev(hess, "hess", torch.float32),
-                                float(perc_damp), _dev(out, "out", torch.uint8), _dev(status, "status", torch.int32),
-                                _stream())
+                                float(perc_damp), _dev(out, "out", torch.uint8), _dev(payload, "payload", torch.uint8),
+                                _dev(status, "status", torch.int32), _stream())
     _check(rc, "iq_choice_search")
-    return out
+    return out if payload is None else (out, payload)
 
 
 def time_next_search(start, stop):

@@ -134,7 +134,7 @@ int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, in
 
 int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
                      const float *grid, const float *importance, const float *hess, float perc_damp,
-                     uint8_t *choices, int32_t *status, hipStream_t stream) {
+                     uint8_t *choices, uint8_t *out, int32_t *status, hipStream_t stream) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
   if (!grid || (rows != 0 && (!w || !hess || !choices))) return IQ_ERR_NULL;
@@ -152,6 +152,7 @@ int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t co
   A.nb = static_cast<int>(cols / 256);
   A.grid = grid;
   A.imp = importance;
+  A.out = out;
   A.status = status;
   const int64_t wgg = (fmt == IQ_FMT_IQ1_M) ? 8 : 4;
   const int64_t total = A.E * ((rows_per_expert + 63) / 64) * A.nb * (32 / wgg);

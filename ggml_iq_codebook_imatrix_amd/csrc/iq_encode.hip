@@ -452,6 +452,7 @@ template <int F, int MODE>
 constexpr int search_min_waves() {
   return (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_S || F == IQ1_S) ? 5
          : (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_XXS || F == IQ2_XS) ? 4
+         : F == IQ1_M                                                                  ? 4
                                                                                        : 1;
 }
 
@@ -953,6 +954,9 @@ __device__ __forceinline__ void record_values(float d, uint32_t rec, const float
 // other wave v forms its part H_uv dw_v; the waves add the parts in unit order
 // (each a slice of the rows of r); the waves score unit u's choices between
 // them, with u's weights passed through LDS; wave u takes the first minimum.
+// With A.out set, the workgroup then packs its block's payload under the
+// picks from the same field records (the every-choice sweep's fields under
+// choice c are the fixed-choice encoder's fields under c).
 template <int F>
 __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncArgs A, const uint32_t *__restrict__ rec,
                                                                           const uint16_t *__restrict__ dblk,
@@ -965,6 +969,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   constexpr int NCW = (NC + U - 1) / U;     // choices of the revisited unit scored per wave
   constexpr int NI = (UV + U - 1) / U;      // cross-term rows summed per wave
   static_assert(NC % CB == 0 && U * NC <= U * UV, "choice batches; the error table fits the parts buffer");
+  static_assert(32 * 64 * 3 + U * 64 <= U * UV * 64 * 4, "the payload fields fit the parts buffer");
   // s_buf holds the table of own-block errors [unit][choice][row] after step A,
   // then the parts H_uv dw_v [v][i][row] of the unit being revisited
   __shared__ float s_buf[U * UV * 64];
@@ -1163,6 +1168,29 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
     }
   }
   if (valid) choices[(r * A.nb + b) * U + v] = static_cast<uint8_t>(pick);
+  if (!A.out) return;
+
+  // payload under the picks: each wave stages its unit's fields (the parts
+  // buffer is free: its last reader is two barriers back), then wave sb packs
+  // sub-block sb as the search kernel does
+  constexpr int WGG = G::WGG, SBS = 32 / WGG, UPW = WGG / GPU;
+  uint16_t(*p_k)[64] = reinterpret_cast<uint16_t(*)[64]>(s_buf);
+  uint8_t(*p_m)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2);
+  uint8_t(*p_c)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2 + 32 * 64 / 4);
+  const uint16_t d16 = dblk[r * A.nb + b];
+#pragma unroll
+  for (int gi = 0; gi < GPU; ++gi) {
+    const uint32_t wd = rrow[pick * cstride + (v * GPU + gi) * rstride];
+    p_k[v * GPU + gi][lane] = static_cast<uint16_t>(wd & 2047u);
+    p_m[v * GPU + gi][lane] = static_cast<uint8_t>(G::IQ1 ? (wd >> 23) & 1u : (wd >> 11) & 255u);
+  }
+  p_c[v][lane] = static_cast<uint8_t>(d16 ? pick : 0);
+  __syncthreads();
+  if (v < SBS && valid) {
+    uint8_t *blk = A.out + (r * A.nb + b) * G::BYTES;
+    pack_bytes<F>(blk, v, lane, p_k + v * WGG, p_m + v * WGG, p_c + v * UPW, d16);
+    if (F != IQ1_M && v == 0) *reinterpret_cast<uint16_t *>(blk) = d16;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1267,6 +1295,8 @@ static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp,
   float *lam = reinterpret_cast<float *>(static_cast<char *>(scratch) + loff);
   EncArgs E = A;
   E.choices = nullptr;
+  E.out = nullptr;
+  E.copies = 0;
   E.rec = rec;
   E.d_out = dblk;
   int rc = launch_quantize_t<F>(E, RECORDS, stream);

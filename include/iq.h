@@ -180,14 +180,18 @@ int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, in
  *  perc_damp  H_b + perc_damp * mean(diag H_b) * I is used (0.3 in [3158]).
  *  choices  (device) [rows, cols/256, choice_groups] uint8 OUT: the picks, to be
  *           passed to iq_quantize (IQ1_S: (delta_sign << 3) | local scale).
+ *  out      (device, nullable) [rows, cols/256, block_bytes] uint8 OUT: when
+ *           given, the payload under the picks -- byte for byte what iq_quantize
+ *           writes with `choices` -- packed from the every-choice fields the
+ *           search already holds, so no second sweep is needed.
  *  importance, grid, w, rows_per_expert, status: as iq_quantize (the codebook
  *  search keeps the importance weighting).
  * Errors: as iq_quantize, plus IQ_ERR_NULL (hess, choices) and IQ_ERR_ARG
  * (perc_damp negative or not finite). */
 int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
                      int64_t rows_per_expert, const float *grid, const float *importance,
-                     const float *hess, float perc_damp, uint8_t *choices, int32_t *status,
-                     hipStream_t stream);
+                     const float *hess, float perc_damp, uint8_t *choices, uint8_t *out,
+                     int32_t *status, hipStream_t stream);
 
 /* Hessian diagonal blocks for iq_choice_search ([3157] series, squashed #3158
  * "local_hessian for GGML IQ": the layer-output error is measured under the

@@ -71,7 +71,7 @@ def test_host_validation_quantize(api):
                                                                       None, None)
     assert ev(fmt=7) == -1 and ev(cols=100) == -4 and ev(out=None) == -3
     cs = lambda fmt=0, hess=FAKE, ch=FAKE, damp=0.3, rpe=64: L.iq_choice_search(fmt, FAKE, 1, 64, 512, rpe, FAKE, None,
-                                                                              hess, damp, ch, None, None)
+                                                                              hess, damp, ch, None, None, None)
     assert cs(fmt=9) == -1 and cs(hess=None) == -3 and cs(ch=None) == -3 and cs(rpe=7) == -4
     assert cs(damp=-1.0) == -5 and cs(damp=float("inf")) == -5
     assert L.iq_format_info(0, None) == -3

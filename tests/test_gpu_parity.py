@@ -212,6 +212,13 @@ def test_choice_search_parity(api, orc, fmt):
     p = host(api.quantize(fmt, dev_w(w, "bf16"), dev(grid), dev(imp), rows_per_expert=rpe, choices=dev(got)))
     pw, _ = orc.quantize(fmt, w, grid, imp, rows_per_expert=rpe, choices=want)
     assert np.array_equal(p, pw)
+    # the payload written with the picks is that encoder's, byte for byte
+    ch2, pay = api.choice_search(fmt, dev_w(w, "bf16"), dev(grid), dev(hess), dev(imp), rows_per_expert=rpe,
+                                 perc_damp=0.3, payload=True)
+    assert np.array_equal(host(ch2), want)
+    pay = host(pay)
+    bad = np.argwhere((pay != pw).any(axis=-1))
+    assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -222,9 +229,11 @@ def test_choice_search_f32_flat(api, orc, fmt):
     rows, cols = 77, 256
     w = inputs.weight(rows, cols, 2500, 2501, bf16=False)
     hess = _correlated_hessian(1, 1, 200, 2502)
-    got = host(api.choice_search(fmt, dev(w), dev(grid), dev(hess)))
+    got, pay = api.choice_search(fmt, dev(w), dev(grid), dev(hess), payload=True)
     want, _ = orc.choice_search(fmt, w, grid, hess)
-    assert np.array_equal(got, want)
+    assert np.array_equal(host(got), want)
+    pw, _ = orc.quantize(fmt, w, grid, None, choices=want)
+    assert np.array_equal(host(pay), pw)
 
 
 @pytest.mark.parametrize("fmt", ["IQ2_XS", "IQ1_M"])
@@ -239,12 +248,15 @@ def test_choice_search_full_size_sampled(api, orc, fmt):
     hess64, _ = orc.hessian_collect(x)
     hess = hess64.astype(np.float32)
     del hess64
-    got = host(api.choice_search(fmt, dev_w(w, "bf16"), dev(grid), dev(hess), dev(imp)))
+    got, pay = api.choice_search(fmt, dev_w(w, "bf16"), dev(grid), dev(hess), dev(imp), payload=True)
+    got, pay = host(got), host(pay)
     rid = np.sort(inputs.rng(2400).choice(w.shape[0], 8, replace=False))
     rid[-1] = w.shape[0] - 1
     want, _ = orc.choice_search(fmt, w, grid, hess, imp, row_ids=rid, threads=16)
     bad = np.argwhere(got[rid] != want)
     assert bad.size == 0, f"{len(bad)} picks differ, first {bad[:5].tolist()}"
+    pw, _ = orc.quantize(fmt, w[rid], grid, imp, choices=want)
+    assert np.array_equal(pay[rid], pw)
 
 
 def test_empty_inputs(api):
@@ -260,8 +272,9 @@ def test_empty_inputs(api):
         ev = api.quantize_every_choice(fmt, w, grid)
         assert tuple(ev.shape) == (info["num_choices"], 0, 2, info["block_bytes"])
         hess = torch.zeros((0, 2, 256, 256), dtype=torch.float32, device="cuda")
-        ch = api.choice_search(fmt, w, grid, hess)
+        ch, pay = api.choice_search(fmt, w, grid, hess, payload=True)
         assert tuple(ch.shape) == (0, 2, info["choice_groups"])
+        assert tuple(pay.shape) == (0, 2, info["block_bytes"])
         y = api.dequantize(fmt, p, grid)
         assert tuple(y.shape) == (0, 512)
     x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
