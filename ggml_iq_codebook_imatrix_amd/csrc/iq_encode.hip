@@ -932,6 +932,59 @@ __device__ __forceinline__ void record_values(float d, uint32_t rec, const float
   group_values<F>(d, rec & 2047u, (rec >> 11) & 255u, (rec >> 19) & 15u, (rec >> 23) & 1u, grid, y);
 }
 
+// The same values in two steps, so the grid loads can be issued well before
+// the values are needed: record_entry fetches the entry, record_finish applies
+// the scale and signs (or shift) exactly as group_values does.
+__device__ __forceinline__ void record_entry(uint32_t rec, const float *__restrict__ grid, float gv[8]) {
+  load_entry(grid + static_cast<int64_t>(rec & 2047u) * 8, gv);
+}
+template <int F>
+__device__ __forceinline__ void record_finish(float d, uint32_t rec, const float gv[8], float y[8]) {
+  using G = Geo<F>;
+  const uint32_t mask = (rec >> 11) & 255u, ls = (rec >> 19) & 15u, h = (rec >> 23) & 1u;
+  if (!G::IQ1) {
+    const float s = d * (static_cast<float>(2 * ls + 1) * 0.125f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = s * gv[j];
+      y[j] = ((mask >> j) & 1u) ? -v : v;
+    }
+  } else {
+    const float s = d * static_cast<float>(2 * ls + 1);
+    const float delta = h ? -0.125f : 0.125f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = s * (gv[j] + delta);
+  }
+}
+
+
+// acc = fmaf(h_n, d[n], acc) for n = 0..15 in order, where h_n is the value
+// lane n of this lane's 16-lane row holds in h (a DPP row broadcast feeds each
+// FMA, so a wave-uniform operand costs no LDS or scalar traffic).  The leading
+// s_nop covers the wait states a DPP read needs after a VALU write of h.
+__device__ __forceinline__ float fmac_row_bcast16(float acc, float h, const float *d) {
+  asm("s_nop 1\n"
+      "v_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %11 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %12 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %13 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %14 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %0, %1, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      : "+v"(acc)
+      : "v"(h), "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5]), "v"(d[6]), "v"(d[7]), "v"(d[8]), "v"(d[9]), "v"(d[10]), "v"(d[11]), "v"(d[12]), "v"(d[13]), "v"(d[14]), "v"(d[15]));
+  return acc;
+}
+
 // Local-Hessian choice search (ModelOpt PR #3158's choice_search): from the
 // payloads of every choice, give each unit its best choice under its own
 // damped diagonal Hessian block, then revisit the units twice, each taking the
@@ -1073,37 +1126,56 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
 #pragma unroll
   for (int t = 0; t < HV4; ++t) reinterpret_cast<float4 *>(s_h)[threadIdx.x + t * NT] = hpre[t];
   __syncthreads();
+  // the fields of this wave's share of a revisited unit's choices do not
+  // depend on the picks: they are loaded one revisit ahead, and their grid
+  // entries are fetched as the revisit starts, to be used after the cross term
+  uint32_t rc[NCW][GPU];
+#pragma unroll
+  for (int k = 0; k < NCW; ++k)
+#pragma unroll
+    for (int gi = 0; gi < GPU; ++gi) rc[k][gi] = v + U * k < NC ? rrow[(v + U * k) * cstride + gi * rstride] : 0u;
   // two passes over the units in ascending order
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll 1
     for (int u = 0; u < U; ++u) {
       const bool more = pass == 0 || u + 1 < U;  // a next revisit exists
+      const int un = (u + 1) % U;
       if (more) {
-        const float4 *src = reinterpret_cast<const float4 *>(H + ((u + 1) % U) * HROW);
+        const float4 *src = reinterpret_cast<const float4 *>(H + un * HROW);
 #pragma unroll
         for (int t = 0; t < HV4; ++t) hpre[t] = src[threadIdx.x + t * NT];
       }
-      // the fields of this wave's share of unit u's choices do not depend on
-      // the picks: their loads are issued before the parts are formed
-      uint32_t rc[NCW][GPU];
+      // (the 32-column units score two choices per wave: their entries would
+      // not fit the register budget, so they are fetched when scored)
+      constexpr bool EARLY = NCW * UV <= 16;
+      float gvc[NCW][UV];
+      if (EARLY) {
+#pragma unroll
+        for (int k = 0; k < NCW; ++k)
+#pragma unroll
+          for (int gi = 0; gi < GPU; ++gi) record_entry(rc[k][gi], A.grid, &gvc[k][gi * 8]);
+      }
+      uint32_t rcn[NCW][GPU];
 #pragma unroll
       for (int k = 0; k < NCW; ++k)
 #pragma unroll
         for (int gi = 0; gi < GPU; ++gi)
-          rc[k][gi] = v + U * k < NC ? rrow[(v + U * k) * cstride + (u * GPU + gi) * rstride] : 0u;
+          rcn[k][gi] = more && v + U * k < NC ? rrow[(v + U * k) * cstride + (un * GPU + gi) * rstride] : 0u;
       if (v != u) {
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
-          const float *Hi = s_h + i * 256 + v * UV;
           float part = 0.0f;
 #pragma unroll
-          for (int j = 0; j < UV; ++j) part = __builtin_fmaf(Hi[j], dwv[j], part);
+          for (int jh = 0; jh < UV / 16; ++jh)
+            part = fmac_row_bcast16(part, s_h[i * 256 + v * UV + jh * 16 + (lane & 15)], dwv + jh * 16);
           s_buf[(v * UV + i) * 64 + lane] = part;
         }
-      } else {
+      } else {  // the unit's weights, reloaded rather than kept in registers
+        float xu[UV];
+        unit_weights<F>(A, r, b, v, xu);
 #pragma unroll
-        for (int i = 0; i < UV; ++i) s_x[i][lane] = xv[i];
+        for (int i = 0; i < UV; ++i) s_x[i][lane] = xu[i];
       }
       __syncthreads();
       if (more) {  // every wave has formed its part: the next revisit's rows replace these
@@ -1115,9 +1187,12 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
       for (int t = 0; t < NI; ++t) {
         const int i = v + U * t;
         if (i < UV) {
+          float pv[U];
+#pragma unroll
+          for (int w = 0; w < U; ++w) pv[w] = s_buf[(w * UV + i) * 64 + lane];  // [u] unused
           float acc = 0.0f;
-          for (int w = 0; w < U; ++w)
-            if (w != u) acc = acc + s_buf[(w * UV + i) * 64 + lane];
+#pragma unroll
+          for (int w = 0; w < U; ++w) acc = w != u ? acc + pv[w] : acc;
           s_r[i][lane] = acc;
         }
       }
@@ -1134,7 +1209,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
 #pragma unroll
           for (int gi = 0; gi < GPU; ++gi) {
             float y[8];
-            record_values<F>(d, rc[k][gi], A.grid, y);
+            if (!EARLY) record_entry(rc[k][gi], A.grid, &gvc[k][gi * 8]);
+            record_finish<F>(d, rc[k][gi], &gvc[k][gi * 8], y);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               dwc[k][gi * 8 + j] = s_x[gi * 8 + j][lane] - y[j];
@@ -1165,6 +1241,10 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
 #pragma unroll
         for (int j = 0; j < UV; ++j) dwv[j] = s_r[j][lane];
       }
+#pragma unroll
+      for (int k = 0; k < NCW; ++k)
+#pragma unroll
+        for (int gi = 0; gi < GPU; ++gi) rc[k][gi] = rcn[k][gi];
     }
   }
   if (valid) choices[(r * A.nb + b) * U + v] = static_cast<uint8_t>(pick);
