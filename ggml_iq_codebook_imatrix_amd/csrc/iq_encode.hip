@@ -505,15 +505,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   const int b = colset / SBS, sb = colset % SBS;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  // the rows this wave packs (lane = row)
-  const bool valid_pack = tile * 64 + lane < A.rpe;
-  const int64_t r_pack = e * A.rpe + (valid_pack ? tile * 64 + lane : A.rpe - 1);
   // this thread's item: group gw of the workgroup, row rl of the tile
   int gw = wave, rl = lane;
   bool all_even = false;  // wave-uniform
   if (SORTED) {
+    const int64_t rn = e * A.rpe + (tile * 64 + lane < A.rpe ? tile * 64 + lane : A.rpe - 1);  // lane = row
     float xn[8];
-    load8(A.w, A.dtype, r_pack * A.cols + (static_cast<int64_t>(b) * 32 + sb * WGG + wave) * 8, xn);
+    load8(A.w, A.dtype, rn * A.cols + (static_cast<int64_t>(b) * 32 + sb * WGG + wave) * 8, xn);
     uint32_t neg = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) neg |= (xn[j] < 0.0f ? 1u : 0u) << j;
@@ -550,6 +548,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   const int unit = gi / GPU;                       // unit within the block
 
   const uint16_t d16 = A.dscr[r * A.nb + b];
+  const bool zero_blk = d16 == 0;
   const float d = f16_bits_to_f32(d16);
 
   float x[8], a[8];
@@ -787,16 +786,18 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   int kb;
   uint32_t mfield;
   rescan_chunk<F, CH>(A.grid, SORTED ? &s_g[gw][0] : gt, S, chs, ssel, hsel, kb, mfield);
-  if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
+  if (zero_blk) { kb = 0; mfield = 0; cu = 0; }
 
   // ---- pack ----------------------------------------------------------------
   s_k[gw][rl] = static_cast<uint16_t>(kb);
   s_m[gw][rl] = static_cast<uint8_t>(mfield);
   if (gw % GPU == 0) s_c[uw][rl] = static_cast<uint8_t>(cu);
   __syncthreads();
-  if (wave != 0 || !valid_pack) return;
-  const uint16_t d16p = SORTED ? A.dscr[r_pack * A.nb + b] : d16;
-  pack_bytes<F>(A.out + (r_pack * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, d16p);
+  // wave 0 packs the tile's rows, lane = row (the row and its scale are
+  // recomputed here rather than kept through the sweep)
+  if (wave != 0 || tile * 64 + lane >= A.rpe) return;
+  const int64_t rp = e * A.rpe + tile * 64 + lane;
+  pack_bytes<F>(A.out + (rp * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, A.dscr[rp * A.nb + b]);
 }
 
 // ---------------------------------------------------------------------------
