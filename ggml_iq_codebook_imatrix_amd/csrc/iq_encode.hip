@@ -52,7 +52,9 @@ namespace iq {
 // Workgroup order: the hardware deals consecutive workgroups round robin to the
 // 8 XCDs.  Remap so each XCD gets a contiguous range of logical work (the same
 // column groups over all their row tiles), which keeps each column group's
-// weighted-norm table in one XCD's L2.
+// weighted-norm table in one XCD's L2.  The search kernel orders that range
+// sub-block fastest, so the workgroups that share a block's payload lines run
+// together and their partial writes merge in L2.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total) {
   const int64_t q = total >> 3, r = total & 7;
@@ -498,11 +500,12 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   __shared__ __attribute__((aligned(8))) float s_g[SORTED ? WGG : 1][SORTED ? N + 2 : 1];
 
   const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
-  const int64_t tile = L % A.tiles_per_e;
-  const int64_t q = L / A.tiles_per_e;
-  const int colset = static_cast<int>(q % (static_cast<int64_t>(A.nb) * SBS));
-  const int64_t e = q / (static_cast<int64_t>(A.nb) * SBS);
-  const int b = colset / SBS, sb = colset % SBS;
+  const int sb = static_cast<int>(L % SBS);
+  const int64_t Lt = L / SBS;
+  const int64_t tile = Lt % A.tiles_per_e;
+  const int64_t q = Lt / A.tiles_per_e;
+  const int b = static_cast<int>(q % A.nb);
+  const int64_t e = q / A.nb;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   // this thread's item: group gw of the workgroup, row rl of the tile
