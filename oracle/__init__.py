@@ -52,6 +52,7 @@ def lib():
         L.orc_f16_to_f32.restype = ctypes.c_float
         L.orc_collect.argtypes = [P, i64, i64, P, ci, ci, P, P]
         L.orc_importance.argtypes = [P, P, ci, i64, ctypes.c_float, P]
+        L.orc_merge.argtypes = [P, P, ci, i64, P, P]
         L.orc_hessian_collect.argtypes = [P, i64, i64, P, ci, ci, P]
         L.orc_fixed_mean.argtypes = [P, i64]
         L.orc_fixed_mean.restype = ctypes.c_float
@@ -127,6 +128,19 @@ def hessian_collect(x, ids=None, num_experts: int = 1, hess=None):
         top_k = ids.shape[1]
     st = lib().orc_hessian_collect(_p(x), T, K, _p(ids), top_k, E, _p(hess))
     return hess, st
+
+
+def merge(src_sums, src_counts, sums, counts):
+    """Add one collection's statistics into another's (fp32 sums, int64 counts);
+    returns (sums, counts, status)."""
+    src = _f32(src_sums)
+    sc = np.ascontiguousarray(src_counts, dtype=np.int64)
+    out_s = np.array(sums, dtype=np.float32, copy=True)
+    out_c = np.array(counts, dtype=np.int64, copy=True)
+    E, K = src.shape
+    assert out_s.shape == (E, K) and sc.shape == out_c.shape == (E,)
+    st = lib().orc_merge(_p(src), _p(sc), E, K, _p(out_s), _p(out_c))
+    return out_s, out_c, st
 
 
 def importance(sums32, counts, floor_rel: float = 1e-6):

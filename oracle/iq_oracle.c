@@ -161,6 +161,27 @@ int orc_collect(const float *x, int64_t T, int64_t K, const int32_t *ids, int to
   return st;
 }
 
+/* Merging the statistics of two collections ([coverage] Facts: the GGUF
+ * imatrix format stores each tensor's in_sum2 and counts so that files can be
+ * merged; [2735] "Single rank": statistics of several ranks would be summed).
+ * sums[e][j] = sums[e][j] + src_sums[e][j], one fp32 addition; counts[e] +=
+ * src_counts[e].  A non-finite source sum of an expert the source touched
+ * (src_counts[e] != 0) raises the non-finite bit ([coverage] Facts: only
+ * touched experts are checked). */
+int orc_merge(const float *src_sums, const int64_t *src_counts, int num_experts, int64_t K, float *sums,
+              int64_t *counts) {
+  int st = 0;
+  for (int e = 0; e < num_experts; ++e) {
+    for (int64_t j = 0; j < K; ++j) {
+      float v = src_sums[(int64_t)e * K + j];
+      if (src_counts[e] != 0 && !isfinite(v)) st |= ORC_ST_NONFINITE;
+      sums[(int64_t)e * K + j] = sums[(int64_t)e * K + j] + v;
+    }
+    counts[e] += src_counts[e];
+  }
+  return st;
+}
+
 /* Hessian blocks for the local-Hessian choice search ([3158]: the layer-output
  * error over the 256-column diagonal blocks of the input Hessian X^T X).
  * hess [E][K/256][256][256] fp64, accumulated in place: for each (t, s) with

@@ -162,6 +162,48 @@ def test_collect_moe_histogram_and_sums(orc):
     assert c2[1] == np.bincount(ids2.ravel(), minlength=E)[1]
 
 
+def test_merge_of_two_collections_is_the_collection_of_both(orc):
+    """Merging the fp32 statistics of two token sets ([coverage] Facts: in_sum2
+    and counts per tensor make files mergeable) gives the statistics of the
+    union: counts exactly (histogram of all ids), sums within the rounding of
+    the two fp32 inputs and the one fp32 addition (fp64 closed form)."""
+    T1, T2, K, E, top_k = 190, 77, 48, 12, 2
+    x1 = inputs.activations(T1, K, 3600, 3601, bf16=True)
+    x2 = inputs.activations(T2, K, 3602, 3603, bf16=True)
+    i1 = inputs.routing(T1, top_k, E, 3604, n_idle=2)
+    i2 = inputs.routing(T2, top_k, E, 3605, n_idle=3)
+    s1, c1, _ = orc.collect(x1, i1, E)
+    s2, c2, _ = orc.collect(x2, i2, E)
+    ms, mc, st = orc.merge(s2.astype(np.float32), c2, s1.astype(np.float32), c1)
+    assert st == 0
+    assert np.array_equal(mc, np.bincount(np.concatenate([i1.ravel(), i2.ravel()]), minlength=E))
+    ref = np.zeros((E, K))
+    for x, ids in ((x1, i1), (x2, i2)):
+        for e in range(E):
+            ref[e] += ((ids == e).sum(axis=1)[:, None] * np.square(x.astype(np.float64))).sum(axis=0)
+    u = 2.0 ** -24
+    assert np.all(np.abs(ms.astype(np.float64) - ref) <= 3 * u * ref + 1e-45)
+    # identities that hold exactly in fp32: adding zeros, doubling, commutation
+    z, zc, _ = orc.merge(np.zeros((E, K), np.float32), np.zeros(E, np.int64), s1.astype(np.float32), c1)
+    assert np.array_equal(z, s1.astype(np.float32)) and np.array_equal(zc, c1)
+    d, dc, _ = orc.merge(s1.astype(np.float32), c1, s1.astype(np.float32), c1)
+    assert np.array_equal(d, 2 * s1.astype(np.float32)) and np.array_equal(dc, 2 * c1)
+    ab, _, _ = orc.merge(s1.astype(np.float32), c1, s2.astype(np.float32), c2)
+    assert np.array_equal(ab, ms)
+
+
+def test_merge_flags_nonfinite_only_for_touched_experts(orc):
+    E, K = 4, 16
+    src = np.ones((E, K), np.float32)
+    cnt = np.array([3, 0, 5, 1], np.int64)
+    src[1, 2] = np.nan          # expert 1 untouched by the source: not checked
+    _, _, st = orc.merge(src, cnt, np.zeros((E, K), np.float32), np.zeros(E, np.int64))
+    assert st == 0
+    src[2, 5] = np.inf          # expert 2 touched
+    _, _, st = orc.merge(src, cnt, np.zeros((E, K), np.float32), np.zeros(E, np.int64))
+    assert st == 1
+
+
 def test_hessian_blocks_pinned_by_collector_and_outer_products(orc):
     """Diagonal of each block = the imatrix collector's per-column sum of squares
     (exact in fp64 for bf16 inputs); blocks symmetric; a brute-force sum of
