@@ -29,6 +29,7 @@ SIGNATURES = {
     "iq_format_info": ([_I, _P], _I),
     "iq_imatrix_collect": ([_P, _I, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "iq_hessian_collect": ([_P, _I, _I64, _I64, _P, _I, _I, _I, _P, _P, _P], _I),
+    "iq_imatrix_merge": ([_P, _P, _I, _I64, _P, _P, _P, _P], _I),
     "iq_imatrix_importance": ([_P, _P, _I, _I64, _F, _P, _P, _P], _I),
     "iq_quantize": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
     "iq_quantize_every_choice": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P], _I),
@@ -165,6 +166,22 @@ def hessian_collect(x: torch.Tensor, ids: torch.Tensor | None = None, num_expert
                                   _dev(status, "status", torch.int32), _stream())
     _check(rc, "iq_hessian_collect")
     return hess
+
+
+def imatrix_merge(src_sums: torch.Tensor, src_counts: torch.Tensor, sums: torch.Tensor, counts: torch.Tensor,
+                  status: torch.Tensor | None = None):
+    """Add one collection's statistics into another's in place: sums += src_sums,
+    counts += src_counts.  Returns (sums, counts)."""
+    if src_sums.dim() != 2:
+        raise IQError("src_sums must be [E, K]")
+    E, K = src_sums.shape
+    if tuple(sums.shape) != (E, K) or tuple(src_counts.shape) != (E,) or tuple(counts.shape) != (E,):
+        raise IQError("sums must be [E, K] and counts [E], like the source")
+    rc = lib().iq_imatrix_merge(_dev(src_sums, "src_sums", torch.float32), _dev(src_counts, "src_counts", torch.int64),
+                                E, K, _dev(sums, "sums", torch.float32), _dev(counts, "counts", torch.int64),
+                                _dev(status, "status", torch.int32), _stream())
+    _check(rc, "iq_imatrix_merge")
+    return sums, counts
 
 
 def imatrix_importance(sums: torch.Tensor, counts: torch.Tensor, floor_rel: float = 1e-6,

@@ -87,6 +87,24 @@ int iq_imatrix_importance(const float *sums, const int64_t *counts, int num_expe
              : IQ_ERR_HIP;
 }
 
+int iq_imatrix_merge(const float *src_sums, const int64_t *src_counts, int num_experts, int64_t K, float *sums,
+                     int64_t *counts, int32_t *status, hipStream_t stream) {
+  if (!src_sums || !src_counts || !sums || !counts) return IQ_ERR_NULL;
+  if (num_experts < 1 || K <= 0) return IQ_ERR_ARG;
+  const int64_t n = static_cast<int64_t>(num_experts) * K;
+  if (n / 256 >= (int64_t(1) << 31)) return IQ_ERR_ARG;
+  // in place: the sources may not overlap the accumulators
+  auto overlap = [](const void *a, const void *b, int64_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bytes && y < x + bytes;
+  };
+  if (overlap(src_sums, sums, n * static_cast<int64_t>(sizeof(float))) ||
+      overlap(src_counts, counts, num_experts * static_cast<int64_t>(sizeof(int64_t))))
+    return IQ_ERR_ARG;
+  return iq::launch_merge(src_sums, src_counts, num_experts, K, sums, counts, status, stream) == 0 ? IQ_OK
+                                                                                                 : IQ_ERR_HIP;
+}
+
 static int quantize_common(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
                            const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
                            int32_t *status, bool every, hipStream_t stream) {

@@ -393,6 +393,52 @@ int launch_importance(const float *sums, const int64_t *counts, int E, int64_t K
 }
 
 // ---------------------------------------------------------------------------
+// Merge of two collections' statistics (the GGUF imatrix files keep in_sum2
+// and counts per tensor so that they can be merged; summing ranks' statistics
+// is the same operation): sums[e][j] = sums[e][j] + src[e][j], one fp32
+// addition per element; counts[e] += src_counts[e].  One thread per element,
+// or per 4 elements as one 16-byte access when K and the pointers allow;
+// non-finite source values of an expert the source touched raise the
+// non-finite bit.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ src, const int64_t *__restrict__ src_counts,
+                                                    int E, int64_t K, float *__restrict__ sums,
+                                                    int64_t *__restrict__ counts, bool vec, int32_t *status) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < E) counts[i] += src_counts[i];
+  const int64_t n = static_cast<int64_t>(E) * K;
+  int st = 0;
+  if (vec) {
+    if (4 * i >= n) return;
+    const int64_t e = 4 * i / K;
+    const float4 v = reinterpret_cast<const float4 *>(src)[i];
+    float4 d = reinterpret_cast<float4 *>(sums)[i];
+    if (src_counts[e] != 0 && !(finite_f(v.x) && finite_f(v.y) && finite_f(v.z) && finite_f(v.w)))
+      st = ST_NONFINITE;
+    d.x = d.x + v.x; d.y = d.y + v.y; d.z = d.z + v.z; d.w = d.w + v.w;
+    reinterpret_cast<float4 *>(sums)[i] = d;
+  } else {
+    if (i >= n) return;
+    const float v = src[i];
+    if (src_counts[i / K] != 0 && !finite_f(v)) st = ST_NONFINITE;
+    sums[i] = sums[i] + v;
+  }
+  raise_status(status, st);
+}
+
+int launch_merge(const float *src, const int64_t *src_counts, int E, int64_t K, float *sums, int64_t *counts,
+                 int32_t *status, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(E) * K;
+  const bool vec = (K & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(sums) & 15) == 0;
+  const int64_t threads = vec ? n / 4 : n;
+  const int64_t total = threads > E ? threads : E;
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, stream, src,
+                     src_counts, E, K, sums, counts, vec, status);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------------------------
 // Hessian diagonal blocks for the local-Hessian choice search (ModelOpt PR
 // #3158: the layer-output error is taken over the 256-column diagonal blocks
 // of the input Hessian).  hess[e][b] += sum over the (token, slot) pairs

@@ -39,6 +39,8 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
                    int chunk_rows, float *sums, int64_t *counts, int32_t *status, hipStream_t stream);
 int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
                    int chunk_rows, float *hess, int32_t *status, hipStream_t stream);
+int launch_merge(const float *src, const int64_t *src_counts, int E, int64_t K, float *sums, int64_t *counts,
+                 int32_t *status, hipStream_t stream);
 int launch_importance(const float *sums, const int64_t *counts, int E, int64_t K, float floor_rel,
                       float *imp, int32_t *status, hipStream_t stream);
 

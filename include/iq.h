@@ -110,6 +110,26 @@ int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int
                        int top_k, int num_experts, int chunk_rows, float *sums, int64_t *counts,
                        int32_t *status, hipStream_t stream);
 
+/* Merge of two collections' statistics ([coverage] Facts: the GGUF imatrix
+ * format stores in_sum2 and counts per tensor so that files can be merged;
+ * [2735] "Single rank": summing the statistics of data-parallel ranks is the
+ * same addition).
+ *
+ *  sums[e][j] = sums[e][j] + src_sums[e][j] (one fp32 addition, round to
+ *  nearest even); counts[e] += src_counts[e] (exact).  Merging in a fixed
+ *  order therefore repeats bit for bit; merges in different orders agree
+ *  within the fp32 rounding of each addition.
+ *  src_sums (device) [E, K] f32, src_counts (device) [E] int64: read only,
+ *           e.g. a collection loaded from a statistics file.
+ *  sums, counts (device) [E, K] f32 and [E] int64, ACCUMULATED in place.
+ *  status   (device, nullable): IQ_STATUS_NONFINITE when a source sum of an
+ *           expert with src_counts[e] != 0 is not finite (the value is still
+ *           added; experts the source did not touch are not checked).
+ * Errors: IQ_ERR_NULL (any array), IQ_ERR_ARG (E < 1, K <= 0, or a source
+ * array overlapping its accumulator). */
+int iq_imatrix_merge(const float *src_sums, const int64_t *src_counts, int num_experts, int64_t K,
+                     float *sums, int64_t *counts, int32_t *status, hipStream_t stream);
+
 /* Importance from collected statistics ([2735] "What imatrix does" and "Why
  * the square root": the search weight is sqrt(E[x_j^2]), floored ("Shared
  * floor"); [coverage] Facts: counts[e] == 0 gives weight 1 on every channel).

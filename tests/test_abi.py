@@ -31,7 +31,8 @@ def api():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["iq_format_info", "iq_imatrix_collect", "iq_hessian_collect", "iq_imatrix_importance", "iq_quantize",
+        ["iq_format_info", "iq_imatrix_collect", "iq_hessian_collect", "iq_imatrix_merge", "iq_imatrix_importance",
+         "iq_quantize",
          "iq_quantize_every_choice", "iq_choice_search", "iq_dequantize", "iq_time_next_search",
          "iq_error_string"])
 
@@ -99,6 +100,13 @@ def test_host_validation_collect_importance_decode(api):
                                                                                        None, None)
     assert imp(s=None) == -3 and imp(out=None) == -3
     assert imp(E=0) == -5 and imp(K=0) == -5 and imp(fl=-1.0) == -5 and imp(fl=float("nan")) == -5
+    F2, F3 = ctypes.c_void_p(0x2000), ctypes.c_void_p(0x9000)
+    m = lambda s=FAKE, sc=F2, E=2, K=8, d=F3, dc=ctypes.c_void_p(0xA000): L.iq_imatrix_merge(s, sc, E, K, d, dc,
+                                                                                            None, None)
+    assert m(s=None) == -3 and m(sc=None) == -3 and m(d=None) == -3 and m(dc=None) == -3
+    assert m(E=0) == -5 and m(K=0) == -5
+    assert m(d=ctypes.c_void_p(0x1020)) == -5      # source sums overlap the accumulator
+    assert m(dc=ctypes.c_void_p(0x2008)) == -5     # source counts overlap the accumulator
     d = lambda fmt=0, p=FAKE, rows=4, cols=256, grid=FAKE, out=FAKE, dt=0: L.iq_dequantize(
         fmt, p, rows, cols, grid, out, dt, None)
     assert d(fmt=9) == -1 and d(dt=3) == -2 and d(p=None) == -3 and d(cols=100) == -4

@@ -388,6 +388,57 @@ def test_collect_flags(api):
     assert host(counts).tolist() == [63, 64, 0, 0]
 
 
+@pytest.mark.parametrize("K", [2048, 2048 + 3])
+def test_merge_parity(api, orc, K):
+    """Merged statistics bit-exact against the oracle's fp32 additions (16-byte
+    path and scalar path), counts exact, the non-finite flag only for touched
+    experts; the accumulators' offset views take the scalar path."""
+    say("merge", K)
+    E = 11
+    g = inputs.rng(1750 + K)
+    dst = (g.lognormal(0, 2, (E, K)) * 30).astype(np.float32)
+    src = (g.lognormal(0, 2, (E, K)) * 30).astype(np.float32)
+    dcnt = g.integers(0, 5000, E).astype(np.int64)
+    scnt = g.integers(0, 5000, E).astype(np.int64)
+    scnt[3] = 0
+    src[3, 7] = np.nan                     # untouched by the source: not flagged
+    want_s, want_c, st_o = orc.merge(src, scnt, dst, dcnt)
+    sums, counts, st = dev(dst), dev(dcnt), api.new_status()
+    api.imatrix_merge(dev(src), dev(scnt), sums, counts, status=st)
+    assert int(host(st)[0]) == st_o == 0
+    assert np.array_equal(host(counts), want_c)
+    assert np.array_equal(host(sums).view(np.uint32), want_s.view(np.uint32))
+    # a touched non-finite source value; accumulators at a 4-byte offset
+    src[5, 1] = np.inf
+    want_s, want_c, st_o = orc.merge(src, scnt, dst, dcnt)
+    buf = torch.zeros(E * K + 1, dtype=torch.float32, device="cuda")
+    sums = buf[1:].view(E, K)
+    sums.copy_(dev(dst))
+    counts, st = dev(dcnt), api.new_status()
+    api.imatrix_merge(dev(src), dev(scnt), sums, counts, status=st)
+    assert int(host(st)[0]) == st_o == 1
+    assert np.array_equal(host(sums).view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(host(counts), want_c)
+
+
+def test_merge_of_split_collection(api, orc):
+    """Collecting two token halves and merging them equals collecting all the
+    tokens (counts exact; sums within the 1e-5 collection bar of the oracle's
+    fp64 sums over all tokens), for routed experts."""
+    say("merge of split collection")
+    T, K, E = 3000, 512, 16
+    x = inputs.activations(T, K, 1760, 1761, bf16=True)
+    ids = inputs.routing(T, 4, E, 1762, n_idle=3)
+    xd, idd = dev_w(x, "bf16"), dev(ids)
+    s1, c1 = api.imatrix_collect(xd[:1100], idd[:1100], E)
+    s2, c2 = api.imatrix_collect(xd[1100:], idd[1100:], E)
+    api.imatrix_merge(s2, c2, s1, c1)
+    want_s, want_c, _ = orc.collect(x, ids, E)
+    assert np.array_equal(host(c1), want_c)
+    got = host(s1).astype(np.float64)
+    assert np.all(np.abs(got - want_s) <= 1e-5 * want_s)
+
+
 def test_importance_parity(api, orc):
     say("importance")
     E, K = 9, 2048 + 5
