@@ -439,6 +439,102 @@ int launch_merge(const float *src, const int64_t *src_counts, int E, int64_t K, 
 }
 
 // ---------------------------------------------------------------------------
+// Routed token lists (for the Hessian blocks): each expert's member tokens in
+// ascending order, built once from the routing bitmaps, so that a wave reads
+// its next tokens with one coalesced load instead of walking bitmap words.
+// An entry is the token index, with bit 31 set when the token names the
+// expert more than once (the reader then repeats it).  lstart[e] is the
+// expert's first entry, lstart[E] the total.
+// ---------------------------------------------------------------------------
+// entries per expert: one wave per expert, popcounts of its bitmap words
+__global__ void __launch_bounds__(256) route_count_kernel(const uint32_t *__restrict__ bm, int64_t nchunks, int E,
+                                                           int W, int64_t *__restrict__ lens) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= E) return;
+  int64_t n = 0;
+  for (int64_t i = lane; i < nchunks * W; i += 64) {
+    const int64_t c = i / W, q = i % W;
+    n += __builtin_popcount(bm[(c * E + e) * W + q]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+  if (lane == 0) lens[e] = n;
+}
+
+// lstart = exclusive prefix sum of lens (one workgroup of 1,024 threads, each a
+// contiguous run of experts)
+__global__ void __launch_bounds__(1024) route_scan_kernel(const int64_t *__restrict__ lens, int E,
+                                                          int64_t *__restrict__ lstart) {
+  __shared__ int64_t s_part[1024];
+  const int per = (E + 1023) / 1024;
+  const int e0 = threadIdx.x * per, e1 = e0 + per < E ? e0 + per : E;
+  int64_t own = 0;
+  for (int e = e0; e < e1; ++e) own += lens[e];
+  s_part[threadIdx.x] = own;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan over the 1,024 runs
+    const int64_t v = threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
+    __syncthreads();
+    s_part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int64_t run = s_part[threadIdx.x] - own;
+  for (int e = e0; e < e1; ++e) {
+    lstart[e] = run;
+    run += lens[e];
+  }
+  if (threadIdx.x == 1023) lstart[E] = s_part[1023];
+}
+
+// the lists: one workgroup per expert walks its bitmap words in token order,
+// 256 words at a time (a word per thread, positions by a workgroup scan of the
+// popcounts), and writes each member with its repeat flag
+__global__ void __launch_bounds__(256) route_list_kernel(const uint32_t *__restrict__ bm,
+                                                          const uint8_t *__restrict__ dup, int64_t nchunks, int E,
+                                                          int W, int chunk_rows, const int64_t *__restrict__ lstart,
+                                                          uint32_t *__restrict__ list) {
+  __shared__ int s_w[4];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t base = lstart[e];
+  const int64_t nw = nchunks * W;
+  for (int64_t i0 = 0; i0 < nw; i0 += 256) {
+    const int64_t i = i0 + threadIdx.x;
+    uint32_t bits = 0u;
+    int64_t c = 0, q = 0;
+    if (i < nw) {
+      c = i / W;
+      q = i % W;
+      bits = bm[(c * E + e) * W + q];
+    }
+    const int n = __builtin_popcount(bits);
+    int incl = n;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      before += w < wave ? s_w[w] : 0;
+      total += s_w[w];
+    }
+    int64_t pos = base + before + incl - n;
+    const int64_t t0 = c * chunk_rows + q * 32;
+    for (uint32_t b = bits; b; b &= b - 1u) {
+      const int64_t t = t0 + __builtin_ctz(b);
+      list[pos++] = static_cast<uint32_t>(t) | (dup[t] ? 0x80000000u : 0u);
+    }
+    base += total;
+    __syncthreads();  // s_w is rewritten by the next round
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Hessian diagonal blocks for the local-Hessian choice search (ModelOpt PR
 // #3158: the layer-output error is taken over the 256-column diagonal blocks
 // of the input Hessian).  hess[e][b] += sum over the (token, slot) pairs
@@ -463,9 +559,10 @@ constexpr int kHTok = 32;  // tokens per step
 template <int DT>
 __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x, int64_t T, int64_t K,
                                                      const int32_t *__restrict__ ids, int top_k, int E,
-                                                     int chunk_rows, int W, const uint32_t *__restrict__ bm,
-                                                     const uint8_t *__restrict__ dup, int64_t split_len,
-                                                     float *__restrict__ dst, bool accumulate, int32_t *status) {
+                                                     const uint32_t *__restrict__ list,
+                                                     const int64_t *__restrict__ lstart, int64_t nsplit,
+                                                     int64_t split_len, float *__restrict__ dst, bool accumulate,
+                                                     int32_t *status) {
   constexpr int RS = DT == 1 ? 40 : 33;  // LDS row: 32 tokens + padding (bf16 80 B, f32 132 B)
   using elem_t = typename std::conditional<DT == 1, uint16_t, float>::type;
   __shared__ __attribute__((aligned(16))) elem_t sA[64][RS];
@@ -484,8 +581,13 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
   const int tj = ti + tp;
   const int lane = threadIdx.x;
   const int64_t colA = static_cast<int64_t>(b) * 256 + ti * 64, colB = static_cast<int64_t>(b) * 256 + tj * 64;
-  const int64_t t0 = split * split_len;
-  const int64_t t1 = (t0 + split_len < T) ? t0 + split_len : T;
+  // dense: the split's token range; routed: its share of e's token list
+  int64_t t0 = split * split_len, t1 = (t0 + split_len < T) ? t0 + split_len : T;
+  if (ids != nullptr) {
+    const int64_t ls = lstart[e], len = lstart[e + 1] - ls;
+    t0 = ls + split * len / nsplit;
+    t1 = ls + (split + 1) * len / nsplit;
+  }
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -495,15 +597,19 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // token stream.  Dense: the range in order.  Routed: advanced by lane 0 from
-  // the bitmap words (the word being read: its remaining bits, the token of
-  // bit 0 and, per token, whether it names an expert twice), repeating a token
-  // as often as e appears in its ids
-  int64_t tw = t0, wbase = 0, last = 0;
-  uint32_t bits = 0u, dbits = 0u;
-  int pending = 0;
+  // token stream.  Dense: the range in order.  Routed: the list entries
+  // [t0, t1), 32 per batch; their load is issued one batch ahead.  An entry
+  // flagged as naming e more than once sends that batch down a path where lane
+  // 0 repeats the token as often as e appears in its ids.
   int64_t cur = t0;
+  int pending = 0;        // repeats of `last` still to place (routed slow path)
+  int last = 0;
   bool finite = true;
+  uint32_t ent = 0u;      // routed: list entry cur + lane (lanes < 32), loaded ahead
+  auto fetch = [&]() {
+    ent = (ids != nullptr && lane < kHTok && cur + lane < t1) ? list[cur + lane] : 0u;
+  };
+  fetch();
   // next batch of tokens into s_tok; returns how many (uniform)
   auto fill = [&]() -> int {
     int nt = 0;
@@ -513,45 +619,40 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
       cur += nt;
       return nt;
     }
+    const int64_t avail = t1 - cur;
+    const uint64_t flagged = __ballot(lane < kHTok && lane < avail && (ent >> 31));
+    if (pending == 0 && flagged == 0) {
+      nt = static_cast<int>(avail < kHTok ? avail : kHTok);
+      if (lane < kHTok) s_tok[lane] = lane < nt ? static_cast<int>(ent & 0x7fffffffu) : -1;
+      cur += nt;
+      fetch();
+      return nt;
+    }
     if (lane == 0) {
       while (nt < kHTok) {
         if (pending > 0) {
-          s_tok[nt++] = static_cast<int>(last);
+          s_tok[nt++] = last;
           --pending;
           continue;
         }
-        if (bits == 0u) {
-          if (tw >= t1) break;
-          const int64_t ch = tw / chunk_rows, p = tw - ch * chunk_rows;
-          const int sh = static_cast<int>(p & 31);
-          wbase = tw - sh;
-          bits = (bm[(ch * E + e) * W + (p >> 5)] >> sh) << sh;
-          int64_t next = ch * chunk_rows + (p | 31) + 1;
-          if (next > (ch + 1) * chunk_rows) next = (ch + 1) * chunk_rows;
-          if (next > t1) next = t1;
-          if (next - wbase < 32) bits &= (1u << (next - wbase)) - 1u;
-          tw = next;
-          // repeat flags of the word's member tokens, one bit each
-          dbits = 0u;
-          for (uint32_t mb = bits; mb; mb &= mb - 1u) {
-            const int z = __builtin_ctz(mb);
-            dbits |= (dup[wbase + z] ? 1u : 0u) << z;
-          }
-          continue;
-        }
-        const int bit = __builtin_ctz(bits);
-        last = wbase + bit;
-        bits &= bits - 1u;
+        if (cur >= t1) break;
+        const uint32_t en = list[cur++];
+        last = static_cast<int>(en & 0x7fffffffu);
         int mult = 1;
-        if ((dbits >> bit) & 1u) {  // rare: count the repeats of e in this token's ids
+        if (en >> 31) {
           mult = 0;
-          for (int s = 0; s < top_k; ++s) mult += ids[last * top_k + s] == e;
+          for (int s = 0; s < top_k; ++s) mult += ids[static_cast<int64_t>(last) * top_k + s] == e;
         }
-        s_tok[nt++] = static_cast<int>(last);
+        s_tok[nt++] = last;
         pending = mult - 1;
       }
       for (int q = nt; q < kHTok; ++q) s_tok[q] = -1;
     }
+    // lane 0 advanced the stream: every lane takes its state
+    cur = static_cast<int64_t>(__shfl(static_cast<long long>(cur), 0));
+    pending = __shfl(pending, 0);
+    last = __shfl(last, 0);
+    fetch();
     return __shfl(nt, 0);
   };
   // this lane's share of a batch: bf16 -- column pair cp of both tiles for token
@@ -721,7 +822,8 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
   const int W = (chunk_rows + 31) / 32 + 1;
   const int64_t ntiles = static_cast<int64_t>(E) * (K / 256) * 10;
-  // enough waves for 256 CUs, with at least 256 tokens per split
+  // enough waves for 256 CUs, with at least 256 tokens per split (dense) or a
+  // share of each expert's list (routed)
   int64_t nsplit = 1;
   if (ntiles < 2048) {
     nsplit = (2048 + ntiles - 1) / ntiles;
@@ -729,32 +831,51 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
     if (nsplit > by_tokens) nsplit = by_tokens;
     if (nsplit < 1) nsplit = 1;
   }
-  const int64_t split_len = ((T + nsplit - 1) / nsplit + kHTok - 1) / kHTok * kHTok;
-  nsplit = (T + split_len - 1) / split_len;
+  int64_t split_len = T;
+  if (!ids) {
+    split_len = ((T + nsplit - 1) / nsplit + kHTok - 1) / kHTok * kHTok;
+    nsplit = (T + split_len - 1) / split_len;
+  }
   const int64_t hn = static_cast<int64_t>(E) * (K / 256) * 65536;
+  // scratch: split partials; routed: bitmaps, repeat flags, list lengths and starts, lists
+  const size_t pbytes = nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0;
   const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
   const size_t dbytes = ids ? static_cast<size_t>(T) : 0;
-  const size_t pbytes = nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0;
+  const size_t nbytes = ids ? static_cast<size_t>(2 * E + 1) * sizeof(int64_t) : 0;
+  const size_t lbytes = ids ? static_cast<size_t>(T) * top_k * sizeof(uint32_t) : 0;
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  const size_t off_b = up(pbytes), off_d = off_b + up(bbytes), off_n = off_d + up(dbytes), off_l = off_n + up(nbytes);
   void *scratch = nullptr;
-  const size_t off_b = (pbytes + 255) & ~size_t(255), off_d = off_b + ((bbytes + 255) & ~size_t(255));
-  if (off_d + dbytes > 0 && hipMallocAsync(&scratch, off_d + dbytes + 256, stream) != hipSuccess) return -1;
-  float *partial = static_cast<float *>(scratch);
-  uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + off_b) : nullptr;
-  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(static_cast<char *>(scratch) + off_d) : nullptr;
-  if (ids)
+  if (off_l + lbytes > 0 && hipMallocAsync(&scratch, off_l + lbytes + 256, stream) != hipSuccess) return -1;
+  char *base = static_cast<char *>(scratch);
+  float *partial = reinterpret_cast<float *>(base);
+  uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(base + off_b) : nullptr;
+  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(base + off_d) : nullptr;
+  int64_t *lens = ids ? reinterpret_cast<int64_t *>(base + off_n) : nullptr;
+  int64_t *lstart = ids ? lens + E : nullptr;
+  uint32_t *list = ids ? reinterpret_cast<uint32_t *>(base + off_l) : nullptr;
+  if (ids) {
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
                        dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, dup, status);
+    hipLaunchKernelGGL(route_count_kernel, dim3(static_cast<unsigned>((E + 3) / 4)), dim3(256), 0, stream,
+                       static_cast<const uint32_t *>(bm), nchunks, E, W, lens);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, static_cast<const int64_t *>(lens), E,
+                       lstart);
+    hipLaunchKernelGGL(route_list_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream,
+                       static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), nchunks, E, W,
+                       chunk_rows, static_cast<const int64_t *>(lstart), list);
+  }
   float *dst = nsplit > 1 ? partial : hess;
   const bool accumulate = nsplit == 1;
   const dim3 g(static_cast<unsigned>(ntiles * nsplit));
   if (dtype == 1)
-    hipLaunchKernelGGL(hessian_kernel<1>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E, chunk_rows, W,
-                       static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), split_len, dst,
-                       accumulate, status);
+    hipLaunchKernelGGL(hessian_kernel<1>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E,
+                       static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart), nsplit, split_len,
+                       dst, accumulate, status);
   else
-    hipLaunchKernelGGL(hessian_kernel<0>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E, chunk_rows, W,
-                       static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), split_len, dst,
-                       accumulate, status);
+    hipLaunchKernelGGL(hessian_kernel<0>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E,
+                       static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart), nsplit, split_len,
+                       dst, accumulate, status);
   if (nsplit > 1)
     hipLaunchKernelGGL(hessian_combine_kernel, dim3(static_cast<unsigned>((hn + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float *>(partial), nsplit, hn, hess);
