@@ -49,6 +49,33 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def measured_valu_peak(iters: int = 2000) -> dict:
+    """What this GPU sustains for the sweep's instruction forms (independent
+    chains, 8 waves per SIMD, built like the encoder): VGPR-only fp32 FMA, the
+    3-input min, and the candidate mix of two FMAs per 3-input min; in
+    algorithmic ops (FMA 1, 3-input min 2), with the shader clock measured
+    during the run.  From libvalu_peak.so (ggml_iq_codebook_imatrix_amd/peak)."""
+    import ctypes
+    path = os.path.join(ROOT, "ggml_iq_codebook_imatrix_amd", "libvalu_peak.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run the package build first")
+    L = ctypes.CDLL(path)
+    d = ctypes.c_double
+    L.valu_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(d), ctypes.POINTER(d), ctypes.POINTER(d)]
+    L.valu_peak.restype = ctypes.c_int
+    out = {}
+    clocks = []
+    for mode, name in ((0, "fma"), (1, "min3"), (2, "mix")):
+        ops, ins, clk = d(), d(), d()
+        if L.valu_peak(mode, iters, ctypes.byref(ops), ctypes.byref(ins), ctypes.byref(clk)) != 0:
+            raise RuntimeError(f"valu_peak mode {mode} failed")
+        out[f"{name}_TOP_s"] = round(ops.value / 1e12, 2)
+        out[f"{name}_Tinstr_s"] = round(ins.value / 1e12, 2)
+        clocks.append(clk.value)
+    out["clock_GHz"] = round(min(clocks) / 1e9, 3) if min(clocks) > 0 else None
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +173,10 @@ def main() -> int:
     roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_TOPS, 2), "unit": "TOP/s",
                 "frac": round(achieved / PEAK_TOPS, 4), "traffic": traffic,
                 "kernel": "search_kernel<IQ2_XS>", "ops_per_launch": ops, "ms_per_launch": round(search_ms, 4)}
+    meas = measured_valu_peak()
+    meas["frac_of_mix"] = round(achieved / meas["mix_TOP_s"], 4)
+    roofline["measured"] = meas
+    log("measured VALU ceiling", meas)
 
     # ---------------- extras: every layout on the same weight --------------
     extras = {}

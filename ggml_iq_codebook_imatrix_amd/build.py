@@ -2,7 +2,9 @@
 
 hipcc compiles every csrc/*.hip for gfx950 with contraction off (explicit fmaf
 only), no fast math, and packed fp32 instructions disabled, then links the
-shared library.  Runs on a machine without a GPU (cross-compilation).
+shared library.  It also builds libvalu_peak.so from peak/valu_peak.hip (the
+benchmark's measured VALU ceiling; not part of libiq).  Runs on a machine
+without a GPU (cross-compilation).
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libiq.so")
+PEAK_SRC = os.path.join(PKG, "peak", "valu_peak.hip")
+PEAK_LIB = os.path.join(PKG, "libvalu_peak.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("IQ_OFFLOAD_ARCH", "gfx950")
 
@@ -50,8 +54,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PEAK_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *CFLAGS, "-shared", PEAK_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAK_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PEAK_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAK_LIB)
     return LIB
 
 
