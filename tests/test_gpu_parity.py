@@ -497,6 +497,22 @@ def test_hessian_moe_exact(api, orc, chunk_rows, dtype):
     assert np.all(got[counts == 0] == 0) and (counts == 0).sum() == 1
 
 
+def test_hessian_routed_repeats_across_splits(api, orc):
+    """Routed token lists under heavy repetition: most tokens name one expert
+    two or three times, lists split into many shares (few experts, so several
+    splits per tile), a ragged token count; exact on integer activations."""
+    say("hessian routed repeats")
+    T, K, E, top_k = 1003, 256, 3, 4
+    x = _int_acts(T, K, 2650)
+    g = inputs.rng(2651)
+    ids = g.integers(0, E, size=(T, top_k)).astype(np.int32)   # repeats on most tokens
+    ids[::7, :] = 1                                          # some tokens name expert 1 four times
+    got = host(api.hessian_collect(dev_w(x, "bf16"), dev(ids), E, chunk_rows=96))
+    want, st = orc.hessian_collect(x, ids, E)
+    assert st == 0
+    assert np.array_equal(got, want.astype(np.float32))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_hessian_real_values_within_bound(api, orc, dtype):
     say("hessian real values", dtype)
