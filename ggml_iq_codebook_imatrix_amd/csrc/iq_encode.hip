@@ -453,8 +453,7 @@ enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2, RECORDS = 3 };
 template <int F, int MODE>
 constexpr int search_min_waves() {
   return (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_S || F == IQ1_S) ? 5
-         : (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_XXS || F == IQ2_XS) ? 4
-         : F == IQ1_M                                                                  ? 4
+         : F == IQ2_XXS || F == IQ2_XS || F == IQ1_M                                   ? 4
                                                                                        : 1;
 }
 
@@ -492,7 +491,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   // about one wave in three holds only even-parity groups and sweeps without
   // the parity term.  A wave then mixes groups, so the weighted norms come from
   // an LDS copy of the workgroup's tables instead of scalar loads.
-  constexpr bool SORTED = G::PARITY && (MODE == SEARCH || MODE == FIXED_CHOICES);
+  constexpr bool SORTED = G::PARITY;
   __shared__ uint16_t s_items[SORTED ? WGG * 64 : 1];
   __shared__ int s_nodd[SORTED ? WGG : 1];
   // row stride N + 2: the (up to WGG) groups a wave reads per entry pair sit in
@@ -709,12 +708,16 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
       int cu = c;
       if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
       __syncthreads();  // the previous choice's bytes have been read from LDS
-      s_k[wave][lane] = static_cast<uint16_t>(kb);
-      s_m[wave][lane] = static_cast<uint8_t>(mfield);
-      if (wave % GPU == 0) s_c[uw][lane] = static_cast<uint8_t>(cu);
+      s_k[gw][rl] = static_cast<uint16_t>(kb);
+      s_m[gw][rl] = static_cast<uint8_t>(mfield);
+      if (gw % GPU == 0) s_c[uw][rl] = static_cast<uint8_t>(cu);
       __syncthreads();
-      if (wave == 0 && valid)
-        pack_bytes<F>(A.out + c * A.copy_stride + (r * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, d16);
+      // wave 0 packs the tile's rows, lane = row
+      if (wave == 0 && tile * 64 + lane < A.rpe) {
+        const int64_t rp = e * A.rpe + tile * 64 + lane;
+        pack_bytes<F>(A.out + c * A.copy_stride + (rp * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c,
+                      A.dscr[rp * A.nb + b]);
+      }
     }
     return;
   }
