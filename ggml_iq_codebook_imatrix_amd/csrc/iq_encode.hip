@@ -167,6 +167,15 @@ __device__ __forceinline__ void load_entry(const float *p, float g[8]) {
   g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
 }
 
+// IQ2 weighted norm of one entry: the fmaf chain over j = 0..7 (the table pass
+// and the in-lane rescans evaluate it this way, so they hold the same value)
+__device__ __forceinline__ float iq2_norm(const float a[8], const float g[8]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s = __builtin_fmaf(a[j], g[j] * g[j], s);
+  return s;
+}
+
 template <int F>
 __device__ __forceinline__ void gterm_block(int64_t blk, const float *__restrict__ grid,
                                             const float *__restrict__ imp, int64_t ntab, float *__restrict__ gtab) {
@@ -183,10 +192,7 @@ __device__ __forceinline__ void gterm_block(int64_t blk, const float *__restrict
 #pragma unroll
   for (int j = 0; j < 8; ++j) a[j] = imp ? imp[tab * 8 + j] : 1.0f;  // importance row e, columns 8cg..8cg+7
   if (!G::IQ1) {
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s = __builtin_fmaf(a[j], g[j] * g[j], s);
-    gtab[tab * G::N + k] = s;
+    gtab[tab * G::N + k] = iq2_norm(a, g);
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -333,9 +339,10 @@ __device__ __forceinline__ void rescan_chunk(const float *__restrict__ grid, con
 template <int CH>
 __device__ __forceinline__ int lds_entry(int k) { return k * 8 + (k / CH) * 4; }
 
-template <int F, int CH>
-__device__ __forceinline__ void rescan_chunk_lds(const float *s_grid, const float a[8], const GroupState<F> &S,
-                                                 int chs, float ssel, int &kb, uint32_t &mfield) {
+template <int F, int CH, bool TAB>
+__device__ __forceinline__ void rescan_chunk_lds(const float *s_grid, const float *gnorm, const float a[8],
+                                                 const GroupState<F> &S, int chs, float ssel, int &kb,
+                                                 uint32_t &mfield) {
   float bt = __builtin_inff();
   kb = chs * CH;
   const float *base = s_grid + lds_entry<CH>(chs * CH);
@@ -343,9 +350,9 @@ __device__ __forceinline__ void rescan_chunk_lds(const float *s_grid, const floa
   for (int i = 0; i < CH; ++i) {
     float g[8];
     load_entry(base + i * 8, g);
-    float gk = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) gk = __builtin_fmaf(a[j], g[j] * g[j], gk);
+    // the weighted norm: the workgroup's LDS table (TAB), else the same fmaf
+    // chain in the lane
+    const float gk = TAB ? gnorm[chs * CH + i] : iq2_norm(a, g);
     const float t = __builtin_fmaf(ssel, gk, S.term(g));
     if (t < bt) { bt = t; kb = chs * CH + i; }
   }
@@ -678,7 +685,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (LDS_RESCAN) rescan_chunk_lds<F, CH>(s_u, a, S, chs, ssel, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F, CH, SORTED>(s_u, SORTED ? &s_g[gw][0] : s_u, a, S, chs, ssel, kb, mfield);
       else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
       GroupFields f;
       f.d16 = d16;
@@ -703,7 +710,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (LDS_RESCAN) rescan_chunk_lds<F, CH>(s_u, a, S, chs, ssel, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F, CH, SORTED>(s_u, SORTED ? &s_g[gw][0] : s_u, a, S, chs, ssel, kb, mfield);
       else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
       int cu = c;
       if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
