@@ -33,7 +33,9 @@
 // entry and the weighted norm G_k are then the same for all 64 lanes, so they
 // arrive as scalar loads and cost no LDS bandwidth; G_k is precomputed once per
 // (expert, column group) by the preparation kernel and copied to a VGPR per
-// entry so the candidate FMAs can co-issue across waves.  The sweep keeps, per
+// entry so the candidate FMAs can co-issue across waves.  (IQ2_XXS/XS waves
+// take 64 (group, row) items dealt by sign parity instead, and read the norms
+// from an LDS copy of the workgroup's tables.)  The sweep keeps, per
 // slot, a running minimum per chunk of CH entries (v_min3 pairs; CH = 32, 16
 // for IQ2_XXS, 8 in the every-choice sweeps) and the index of the chunk
 // holding the first minimum; after the unit's choice is known the chosen chunk
@@ -493,11 +495,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   __shared__ uint16_t s_k[WGG][64];
   __shared__ uint8_t s_m[WGG][64];
   __shared__ uint8_t s_c[UPW][64];
-  // Parity-sorted items (IQ2_XXS/XS search and fixed encodes): the workgroup's
-  // WGG x 64 (group, row) items are dealt to the waves odd-parity first, so
-  // about one wave in three holds only even-parity groups and sweeps without
-  // the parity term.  A wave then mixes groups, so the weighted norms come from
-  // an LDS copy of the workgroup's tables instead of scalar loads.
+  // Parity-sorted items (IQ2_XXS/XS, every mode): the workgroup's WGG x 64
+  // (group, row) items are dealt to the waves odd-parity first, so about one
+  // wave in three holds only even-parity groups and sweeps without the parity
+  // term.  A wave then mixes groups, so the weighted norms come from an LDS
+  // copy of the workgroup's tables instead of scalar loads (the every-choice
+  // rescans read the same copy), and the LDS field tables are indexed by each
+  // item's group and row.
   constexpr bool SORTED = G::PARITY;
   __shared__ uint16_t s_items[SORTED ? WGG * 64 : 1];
   __shared__ int s_nodd[SORTED ? WGG : 1];
