@@ -49,6 +49,18 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def cpu_model() -> str | None:
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def measured_valu_peak(iters: int = 2000) -> dict:
     """What this GPU sustains for the sweep's instruction forms (independent
     chains, 8 waves per SIMD, built like the encoder): VGPR-only fp32 FMA, the
@@ -350,7 +362,7 @@ def main() -> int:
                          f"{rows} rows; {dt:.1f} s",
                "encode_one_thread": {"value": round(64 * cols / dt1 / 1e6, 4), "unit": "M elem/s",
                                      "sample": f"IQ2_XS encode of the first 64 rows on 1 thread; {dt1:.2f} s"},
-               "host_cpus": os.cpu_count()}
+               "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
         log("cpu baseline", cpu)
 
     line = {
