@@ -976,31 +976,53 @@ __device__ __forceinline__ void record_finish(float d, uint32_t rec, const float
 }
 
 
-// acc = fmaf(h_n, d[n], acc) for n = 0..15 in order, where h_n is the value
-// lane n of this lane's 16-lane row holds in h (a DPP row broadcast feeds each
-// FMA, so a wave-uniform operand costs no LDS or scalar traffic).  The leading
-// s_nop covers the wait states a DPP read needs after a VALU write of h.
-__device__ __forceinline__ float fmac_row_bcast16(float acc, float h, const float *d) {
-  asm("s_nop 1\n"
-      "v_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %11 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %12 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %13 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %14 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
-      "v_fmac_f32_dpp %0, %1, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
-      : "+v"(acc)
-      : "v"(h), "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5]), "v"(d[6]), "v"(d[7]), "v"(d[8]), "v"(d[9]), "v"(d[10]), "v"(d[11]), "v"(d[12]), "v"(d[13]), "v"(d[14]), "v"(d[15]));
-  return acc;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+// One wave's cross-term part on the matrix cores: dst[i * 64 + row] =
+// sum_k h[i][k] dw_row[k] for the unit's UV rows i and the wave's 64 rows
+// (lane = row; dw holds the lane's own row), k ascending from zero.  The fp32
+// MFMA forms that take one k per step (32x32x1 in two blocks, 16x16x1 in four)
+// round each step as one fmaf does, so the result is the fmaf chain
+// part = fmaf(h_ik, dw_k, part) bit for bit.  H's row i is the A operand
+// (lane i of each block holds it, read from hrow + i * SH), dw the B operand,
+// so each block is 32 (16) rows of the wave; the accumulator's element (i, row)
+// sits in register r of lane l as decoded below.
+template <int UV, int SH>
+__device__ __forceinline__ void unit_part_mfma(const float *hrow, const float dw[UV], float *dst, int lane) {
+  const float4 *h4 = reinterpret_cast<const float4 *>(hrow + (lane & (UV - 1)) * SH);
+  if constexpr (UV == 32) {
+    f32x32 acc = {};
+#pragma unroll
+    for (int k4 = 0; k4 < UV / 4; ++k4) {
+      const float4 h = h4[k4];
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(h.x, dw[4 * k4 + 0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(h.y, dw[4 * k4 + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(h.z, dw[4 * k4 + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(h.w, dw[4 * k4 + 3], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int i = 8 * ((r & 15) >> 2) + 4 * (lane >> 5) + (r & 3), row = 32 * (r >> 4) + (lane & 31);
+      dst[i * 64 + row] = acc[r];
+    }
+  } else {
+    static_assert(UV == 16, "units of 16 or 32 columns");
+    f32x16 acc = {};
+#pragma unroll
+    for (int k4 = 0; k4 < UV / 4; ++k4) {
+      const float4 h = h4[k4];
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(h.x, dw[4 * k4 + 0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(h.y, dw[4 * k4 + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(h.z, dw[4 * k4 + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(h.w, dw[4 * k4 + 3], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 4 * (lane >> 4) + (r & 3), row = 16 * (r >> 2) + (lane & 15);
+      dst[i * 64 + row] = acc[r];
+    }
+  }
 }
 
 // Local-Hessian choice search (ModelOpt PR #3158's choice_search): from the
@@ -1022,7 +1044,8 @@ __device__ __forceinline__ float fmac_row_bcast16(float acc, float h, const floa
 // from coalesced loads rather than from packed bytes.  Step A: wave v scores
 // every choice of unit v; the own-block errors do not change between passes,
 // so each wave keeps those of the choices it scores later.  A revisit of unit u: every
-// other wave v forms its part H_uv dw_v; the waves add the parts in unit order
+// other wave v forms its part H_uv dw_v on the matrix cores (unit_part_mfma: the
+// same fmaf chain); the waves add the parts in unit order
 // (each a slice of the rows of r); the waves score unit u's choices between
 // them, with u's weights passed through LDS; wave u takes the first minimum.
 // With A.out set, the workgroup then packs its block's payload under the
@@ -1050,9 +1073,11 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   // the revisited unit's rows of the damped-free block H (UV x 256), staged
   // one revisit ahead: each thread prefetches HV4 float4 into registers at the
   // start of a revisit and stores them once the parts have been formed
-  constexpr int HROW = UV * 256, NT = 64 * U, HV4 = HROW / 4 / NT;
+  // (rows padded to SH floats, so the lanes' operand reads of the parts spread
+  // over the banks)
+  constexpr int HROW = UV * 256, NT = 64 * U, HV4 = HROW / 4 / NT, SH = 256 + 4;
   static_assert(HROW % (4 * NT) == 0, "whole float4 per thread");
-  __shared__ __attribute__((aligned(16))) float s_h[HROW];
+  __shared__ __attribute__((aligned(16))) float s_h[UV * SH];
   const int64_t L = xcd_remap(blockIdx.x, A.total_wg);
   const int64_t tile = L % A.tiles_per_e;
   const int64_t q = L / A.tiles_per_e;
@@ -1142,7 +1167,10 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
 #pragma unroll
   for (int t = 0; t < HV4; ++t) hpre[t] = reinterpret_cast<const float4 *>(H)[threadIdx.x + t * NT];
 #pragma unroll
-  for (int t = 0; t < HV4; ++t) reinterpret_cast<float4 *>(s_h)[threadIdx.x + t * NT] = hpre[t];
+  for (int t = 0; t < HV4; ++t) {
+    const int f = threadIdx.x + t * NT;
+    *reinterpret_cast<float4 *>(s_h + (f >> 6) * SH + 4 * (f & 63)) = hpre[t];
+  }
   __syncthreads();
   // the fields of this wave's share of a revisited unit's choices do not
   // depend on the picks: they are loaded one revisit ahead, and their grid
@@ -1181,14 +1209,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
         for (int gi = 0; gi < GPU; ++gi)
           rcn[k][gi] = more && v + U * k < NC ? rrow[(v + U * k) * cstride + (un * GPU + gi) * rstride] : 0u;
       if (v != u) {
-#pragma unroll
-        for (int i = 0; i < UV; ++i) {
-          float part = 0.0f;
-#pragma unroll
-          for (int jh = 0; jh < UV / 16; ++jh)
-            part = fmac_row_bcast16(part, s_h[i * 256 + v * UV + jh * 16 + (lane & 15)], dwv + jh * 16);
-          s_buf[(v * UV + i) * 64 + lane] = part;
-        }
+        unit_part_mfma<UV, SH>(s_h + v * UV, dwv, s_buf + v * UV * 64, lane);
       } else {  // the unit's weights, reloaded rather than kept in registers
         float xu[UV];
         unit_weights<F>(A, r, b, v, xu);
@@ -1198,7 +1219,10 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
       __syncthreads();
       if (more) {  // every wave has formed its part: the next revisit's rows replace these
 #pragma unroll
-        for (int t = 0; t < HV4; ++t) reinterpret_cast<float4 *>(s_h)[threadIdx.x + t * NT] = hpre[t];
+        for (int t = 0; t < HV4; ++t) {
+          const int f = threadIdx.x + t * NT;
+          *reinterpret_cast<float4 *>(s_h + (f >> 6) * SH + 4 * (f & 63)) = hpre[t];
+        }
       }
       // cross term rows i = v, v + U, ...: the parts added in unit order
 #pragma unroll
