@@ -1025,6 +1025,59 @@ __device__ __forceinline__ void unit_part_mfma(const float *hrow, const float dw
   }
 }
 
+// y = H dw for one choice of the wave's own unit, on the matrix cores, in the
+// lanes' own layout: y[i] = sum_k ha_i[k] dw[k], k ascending from zero (the
+// fmaf chain, bit for bit), where lane l holds in ha the row i = l % UV of the
+// damped block and in dw its own row's residual.  The accumulator's layout is
+// unit_part_mfma's; the exchanges then give every lane all UV values of its own
+// row.  UV = 32: register r holds (i, row) = (8 (r % 16 / 4) + 4 (l / 32) + r % 4,
+// 32 (r / 16) + l % 32), so one permlane32 swap per register pair (r, r + 16)
+// trades the upper lanes' low registers for the lower lanes' high ones, leaving
+// i = 8 (r / 4) + r % 4 in register r and i = 8 (r / 4) + 4 + r % 4 in r + 16.
+// UV = 16: register 4 b + e holds (i, row) = (4 (l / 16) + e, 16 b + l % 16):
+// four lane groups of 4 x 4 tiles, transposed by a permlane32 stage (groups
+// 0 <-> 2, 1 <-> 3) and a permlane16 stage (0 <-> 1, 2 <-> 3), leaving i = r in
+// register r.
+template <int UV>
+__device__ __forceinline__ void unit_hdw_mfma(const float ha[UV], const float dw[UV], float y[UV]) {
+  if constexpr (UV == 32) {
+    f32x32 acc = {};
+#pragma unroll
+    for (int k = 0; k < UV; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(ha[k], dw[k], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[16 + r]), false, false);
+      y[8 * (r >> 2) + (r & 3)] = __uint_as_float(sw[0]);
+      y[8 * (r >> 2) + 4 + (r & 3)] = __uint_as_float(sw[1]);
+    }
+  } else {
+    f32x16 acc = {};
+#pragma unroll
+    for (int k = 0; k < UV; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x1f32(ha[k], dw[k], acc, 0, 0, 0);
+    uint32_t t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = __float_as_uint(acc[r]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(t[4 * b + e], t[4 * (b + 2) + e], false, false);
+        t[4 * b + e] = sw[0];
+        t[4 * (b + 2) + e] = sw[1];
+      }
+#pragma unroll
+    for (int b = 0; b < 4; b += 2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(t[4 * b + e], t[4 * (b + 1) + e], false, false);
+        t[4 * b + e] = sw[0];
+        t[4 * (b + 1) + e] = sw[1];
+      }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) y[r] = __uint_as_float(t[r]);
+  }
+}
+
 // Local-Hessian choice search (ModelOpt PR #3158's choice_search): from the
 // payloads of every choice, give each unit its best choice under its own
 // damped diagonal Hessian block, then revisit the units twice, each taking the
@@ -1042,8 +1095,9 @@ __device__ __forceinline__ void unit_part_mfma(const float *hrow, const float dw
 // The every-choice sweep hands over each group's fields under every choice as
 // one word per (choice, group, row), rows contiguous, so the residuals come
 // from coalesced loads rather than from packed bytes.  Step A: wave v scores
-// every choice of unit v; the own-block errors do not change between passes,
-// so each wave keeps those of the choices it scores later.  A revisit of unit u: every
+// every choice of unit v on the matrix cores (unit_hdw_mfma); the own-block
+// errors do not change between passes, so each wave keeps those of the choices
+// it scores later.  A revisit of unit u: every
 // other wave v forms its part H_uv dw_v on the matrix cores (unit_part_mfma: the
 // same fmaf chain); the waves add the parts in unit order
 // (each a slice of the rows of r); the waves score unit u's choices between
@@ -1059,10 +1113,9 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
                                                                           uint8_t *__restrict__ choices) {
   using G = Geo<F>;
   constexpr int U = G::UNITS, UV = 8 * G::GPU, NC = G::NC, GPU = G::GPU;
-  constexpr int CB = F == IQ1_M ? 2 : 4;    // choices scored together in step A (one pass over H_vv)
   constexpr int NCW = (NC + U - 1) / U;     // choices of the revisited unit scored per wave
   constexpr int NI = (UV + U - 1) / U;      // cross-term rows summed per wave
-  static_assert(NC % CB == 0 && U * NC <= U * UV, "choice batches; the error table fits the parts buffer");
+  static_assert(U * NC <= U * UV, "the error table fits the parts buffer");
   static_assert(32 * 64 * 3 + U * 64 <= U * UV * 64 * 4, "the payload fields fit the parts buffer");
   // s_buf holds the table of own-block errors [unit][choice][row] after step A,
   // then the parts H_uv dw_v [v][i][row] of the unit being revisited
@@ -1095,8 +1148,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   const uint32_t *rrow = rec + static_cast<int64_t>(b) * 32 * rstride + r;
   const int64_t cstride = A.nb * 32 * rstride;
 
-  // step A: every choice of unit v under its own damped block, CB at a time;
-  // the U diagonal sub-blocks H_vv ([v][i][j], U * UV * UV = HROW floats) are
+  // step A: every choice of unit v under its own damped block; the U diagonal sub-blocks H_vv ([v][i][j], U * UV * UV = HROW floats) are
   // staged in s_h first
   for (int t4 = threadIdx.x; t4 < HROW / 4; t4 += NT) {
     const int vv = t4 / (UV * UV / 4), rem = t4 % (UV * UV / 4);
@@ -1109,44 +1161,50 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   const float d = f16_bits_to_f32(dblk[r * A.nb + b]);
   int pick = 0;
   {
+    // one choice at a time on the matrix cores (unit_hdw_mfma); the next
+    // choice's field words and grid entries are fetched while this one's
+    // product runs
+    uint32_t rcs[GPU];
+    float gvs[UV];
+#pragma unroll
+    for (int gi = 0; gi < GPU; ++gi) rcs[gi] = rrow[(v * GPU + gi) * rstride];
+#pragma unroll
+    for (int gi = 0; gi < GPU; ++gi) record_entry(rcs[gi], A.grid, &gvs[gi * 8]);
+    __syncthreads();  // s_h holds every H_vv
+    // this lane's row of the damped block H_vv + lambda I (the A operand)
+    float ha[UV];
+    {
+      const int ia = lane & (UV - 1);
+      const float *Hi = s_h + (v * UV + ia) * UV;
+#pragma unroll
+      for (int k = 0; k < UV; ++k) {
+        const float h = Hi[k];
+        ha[k] = k == ia ? h + lam : h;
+      }
+    }
     float best = 0.0f;
 #pragma unroll 1
-    for (int c0 = 0; c0 < NC; c0 += CB) {
-      float dw[CB][UV];
+    for (int c = 0; c < NC; ++c) {
+      float dw[UV];
 #pragma unroll
-      for (int k = 0; k < CB; ++k) {
+      for (int gi = 0; gi < GPU; ++gi) {
+        float y[8];
+        record_finish<F>(d, rcs[gi], &gvs[gi * 8], y);
 #pragma unroll
-        for (int gi = 0; gi < GPU; ++gi) {
-          float y[8];
-          record_values<F>(d, rrow[(c0 + k) * cstride + (v * GPU + gi) * rstride], A.grid, y);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) dw[k][gi * 8 + j] = xv[gi * 8 + j] - y[j];
-        }
+        for (int j = 0; j < 8; ++j) dw[gi * 8 + j] = xv[gi * 8 + j] - y[j];
       }
-      if (c0 == 0) __syncthreads();  // s_h holds every H_vv
-      float err[CB];
+      const int cn = c + 1 < NC ? c + 1 : c;
 #pragma unroll
-      for (int k = 0; k < CB; ++k) err[k] = 0.0f;
+      for (int gi = 0; gi < GPU; ++gi) rcs[gi] = rrow[cn * cstride + (v * GPU + gi) * rstride];
 #pragma unroll
-      for (int i = 0; i < UV; ++i) {
-        const float *Hi = s_h + (v * UV + i) * UV;
-        float y[CB];
+      for (int gi = 0; gi < GPU; ++gi) record_entry(rcs[gi], A.grid, &gvs[gi * 8]);
+      float yv[UV];
+      unit_hdw_mfma<UV>(ha, dw, yv);
+      float err = 0.0f;
 #pragma unroll
-        for (int k = 0; k < CB; ++k) y[k] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < UV; ++j) {
-          const float h = j == i ? Hi[j] + lam : Hi[j];
-#pragma unroll
-          for (int k = 0; k < CB; ++k) y[k] = __builtin_fmaf(h, dw[k][j], y[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < CB; ++k) err[k] = __builtin_fmaf(dw[k][i], y[k], err[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < CB; ++k) {
-        s_buf[(v * NC + c0 + k) * 64 + lane] = err[k];
-        if (c0 + k == 0 || err[k] < best) { best = err[k]; pick = c0 + k; }
-      }
+      for (int i = 0; i < UV; ++i) err = __builtin_fmaf(dw[i], yv[i], err);
+      s_buf[(v * NC + c) * 64 + lane] = err;
+      if (c == 0 || err < best) { best = err; pick = c; }
     }
   }
 #pragma unroll
