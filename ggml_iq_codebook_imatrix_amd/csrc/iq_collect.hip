@@ -464,27 +464,55 @@ __global__ void __launch_bounds__(256) route_count_kernel(const uint32_t *__rest
 
 // lstart = exclusive prefix sum of lens (one workgroup of 1,024 threads, each a
 // contiguous run of experts)
-__global__ void __launch_bounds__(1024) route_scan_kernel(const int64_t *__restrict__ lens, int E,
-                                                          int64_t *__restrict__ lstart) {
-  __shared__ int64_t s_part[1024];
+__global__ void __launch_bounds__(1024) route_scan_kernel(const int64_t *__restrict__ lens, int E, int64_t target,
+                                                          int64_t *__restrict__ lstart, int64_t *__restrict__ sstart,
+                                                          int64_t *__restrict__ pstart, int32_t *__restrict__ heavy) {
+  // three exclusive scans over the experts: list entries, Hessian splits
+  // (ceil(len / target), at least one) and partial slots (the splits of the
+  // experts cut into more than one); then the cut experts in order
+  __shared__ int64_t s_part[3][1024];
   const int per = (E + 1023) / 1024;
   const int e0 = threadIdx.x * per, e1 = e0 + per < E ? e0 + per : E;
-  int64_t own = 0;
-  for (int e = e0; e < e1; ++e) own += lens[e];
-  s_part[threadIdx.x] = own;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan over the 1,024 runs
-    const int64_t v = threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
-    __syncthreads();
-    s_part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int64_t run = s_part[threadIdx.x] - own;
+  auto nsp = [&](int64_t len) -> int64_t { return len > target ? (len + target - 1) / target : 1; };
+  int64_t own[3] = {0, 0, 0};
   for (int e = e0; e < e1; ++e) {
-    lstart[e] = run;
-    run += lens[e];
+    const int64_t n = nsp(lens[e]);
+    own[0] += lens[e];
+    own[1] += n;
+    own[2] += n > 1 ? n : 0;
   }
-  if (threadIdx.x == 1023) lstart[E] = s_part[1023];
+  for (int k = 0; k < 3; ++k) s_part[k][threadIdx.x] = own[k];
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scans over the 1,024 runs
+    int64_t v[3];
+    for (int k = 0; k < 3; ++k) v[k] = threadIdx.x >= o ? s_part[k][threadIdx.x - o] : 0;
+    __syncthreads();
+    for (int k = 0; k < 3; ++k) s_part[k][threadIdx.x] += v[k];
+    __syncthreads();
+  }
+  int64_t run[3];
+  for (int k = 0; k < 3; ++k) run[k] = s_part[k][threadIdx.x] - own[k];
+  for (int e = e0; e < e1; ++e) {
+    const int64_t n = nsp(lens[e]);
+    lstart[e] = run[0];
+    sstart[e] = run[1];
+    pstart[e] = run[2];
+    run[0] += lens[e];
+    run[1] += n;
+    run[2] += n > 1 ? n : 0;
+  }
+  if (threadIdx.x == 1023) {
+    lstart[E] = s_part[0][1023];
+    sstart[E] = s_part[1][1023];
+    pstart[E] = s_part[2][1023];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // the cut experts, ascending (few: each holds more than target entries)
+    int h = 0;
+    for (int e = 0; e < E; ++e)
+      if (sstart[e + 1] - sstart[e] > 1) heavy[h++] = e;
+    heavy[E] = h;
+  }
 }
 
 // the lists: one workgroup per expert walks its bitmap words in token order,
@@ -560,34 +588,62 @@ template <int DT>
 __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x, int64_t T, int64_t K,
                                                      const int32_t *__restrict__ ids, int top_k, int E,
                                                      const uint32_t *__restrict__ list,
-                                                     const int64_t *__restrict__ lstart, int64_t nsplit,
-                                                     int64_t split_len, float *__restrict__ dst, bool accumulate,
-                                                     int32_t *status) {
+                                                     const int64_t *__restrict__ lstart,
+                                                     const int64_t *__restrict__ sstart,
+                                                     const int64_t *__restrict__ pstart, int64_t nsplit,
+                                                     int64_t split_len, float *__restrict__ hess,
+                                                     float *__restrict__ partial, int32_t *status) {
   constexpr int RS = DT == 1 ? 40 : 33;  // LDS row: 32 tokens + padding (bf16 80 B, f32 132 B)
   using elem_t = typename std::conditional<DT == 1, uint16_t, float>::type;
   __shared__ __attribute__((aligned(16))) elem_t sA[64][RS];
   __shared__ __attribute__((aligned(16))) elem_t sB[64][RS];
   __shared__ int s_tok[kHTok];
   const int64_t nb = K / 256;
-  const int64_t ntiles = static_cast<int64_t>(E) * nb * 10;
-  const int64_t split = blockIdx.x / ntiles;
-  const int64_t rem = blockIdx.x % ntiles;
-  int tp = static_cast<int>(rem % 10);
-  const int64_t eb = rem / 10;
-  const int b = static_cast<int>(eb % nb);
-  const int e = static_cast<int>(eb / nb);
+  // Dense: workgroup = (split, block, tile) with uniform token splits.
+  // Routed: workgroup = (split slot, block, tile); the slots are numbered expert
+  // by expert (sstart), an expert holding ceil(len / target) of them.  One slot:
+  // the expert's whole list, added into hess; several: equal shares of the list,
+  // each written to its own partial slot (pstart) for the combine.
+  int64_t t0, t1, slot_e = 0;
+  int e, b, tp;
+  float *Hdst;
+  bool accumulate;
+  if (ids == nullptr) {
+    const int64_t ntiles = static_cast<int64_t>(E) * nb * 10;
+    const int64_t split = blockIdx.x / ntiles, rem = blockIdx.x % ntiles;
+    tp = static_cast<int>(rem % 10);
+    b = static_cast<int>((rem / 10) % nb);
+    e = static_cast<int>(rem / 10 / nb);
+    t0 = split * split_len;
+    t1 = (t0 + split_len < T) ? t0 + split_len : T;
+    accumulate = nsplit == 1;
+    Hdst = accumulate ? hess + (static_cast<int64_t>(e) * nb + b) * 65536
+                      : partial + ((split * E + e) * nb + b) * 65536;
+  } else {
+    const int64_t slot = blockIdx.x / (nb * 10), rem = blockIdx.x % (nb * 10);
+    if (slot >= sstart[E]) return;  // the grid is sized for the most slots the lists allow
+    tp = static_cast<int>(rem % 10);
+    b = static_cast<int>(rem / 10);
+    int lo = 0, hi = E;  // the expert: sstart[e] <= slot < sstart[e + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sstart[mid] <= slot) lo = mid; else hi = mid;
+    }
+    e = lo;
+    slot_e = slot - sstart[e];
+    const int64_t n = sstart[e + 1] - sstart[e];
+    const int64_t ls = lstart[e], len = lstart[e + 1] - ls;
+    t0 = ls + slot_e * len / n;
+    t1 = ls + (slot_e + 1) * len / n;
+    accumulate = n == 1;
+    Hdst = accumulate ? hess + (static_cast<int64_t>(e) * nb + b) * 65536
+                      : partial + ((pstart[e] + slot_e) * nb + b) * 65536;
+  }
   int ti = 0;
   while (tp >= 4 - ti) { tp -= 4 - ti; ++ti; }
   const int tj = ti + tp;
   const int lane = threadIdx.x;
   const int64_t colA = static_cast<int64_t>(b) * 256 + ti * 64, colB = static_cast<int64_t>(b) * 256 + tj * 64;
-  // dense: the split's token range; routed: its share of e's token list
-  int64_t t0 = split * split_len, t1 = (t0 + split_len < T) ? t0 + split_len : T;
-  if (ids != nullptr) {
-    const int64_t ls = lstart[e], len = lstart[e + 1] - ls;
-    t0 = ls + split * len / nsplit;
-    t1 = ls + (split + 1) * len / nsplit;
-  }
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -785,8 +841,7 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
     nt = nn;
   }
   if (!finite) raise_status(status, ST_NONFINITE);
-  // dst: hess itself (one split, accumulate) or this split's partial blocks
-  float *Hb = dst + ((split * E + e) * nb + b) * 65536;
+  float *Hb = Hdst;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -816,32 +871,74 @@ __global__ void __launch_bounds__(256) hessian_combine_kernel(const float *__res
   hess[i] = hess[i] + s;
 }
 
+// Routed: for each expert cut into several splits (heavy[0 .. heavy[E])),
+// hess += partial[first] + partial[first + 1] + ... in split order.
+__global__ void __launch_bounds__(256) hessian_combine_routed_kernel(const float *__restrict__ partial,
+                                                                     const int64_t *__restrict__ sstart,
+                                                                     const int64_t *__restrict__ pstart,
+                                                                     const int32_t *__restrict__ heavy, int E,
+                                                                     int64_t per_e, float *__restrict__ hess) {
+  const int64_t chunks = (per_e + 255) / 256;
+  const int64_t h = blockIdx.x / chunks;
+  if (h >= heavy[E]) return;
+  const int64_t i = (blockIdx.x % chunks) * 256 + threadIdx.x;
+  if (i >= per_e) return;
+  const int e = heavy[h];
+  const int64_t n = sstart[e + 1] - sstart[e];
+  const float *p = partial + pstart[e] * per_e + i;
+  float s = p[0];
+  for (int64_t k = 1; k < n; ++k) s = s + p[k * per_e];
+  float *d = hess + static_cast<int64_t>(e) * per_e + i;
+  *d = *d + s;
+}
+
 int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
                    int chunk_rows, float *hess, int32_t *status, hipStream_t stream) {
   if (T == 0) return 0;
   const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
   const int W = (chunk_rows + 31) / 32 + 1;
-  const int64_t ntiles = static_cast<int64_t>(E) * (K / 256) * 10;
-  // enough waves for 256 CUs, with at least 256 tokens per split (dense) or a
-  // share of each expert's list (routed)
-  int64_t nsplit = 1;
-  if (ntiles < 2048) {
-    nsplit = (2048 + ntiles - 1) / ntiles;
-    const int64_t by_tokens = (T + 255) / 256;
-    if (nsplit > by_tokens) nsplit = by_tokens;
-    if (nsplit < 1) nsplit = 1;
-  }
-  int64_t split_len = T;
+  const int64_t nb = K / 256;
+  const int64_t ntiles = static_cast<int64_t>(E) * nb * 10;
+  const int64_t per_e = nb * 65536;  // floats of one expert's blocks
+  const int64_t hn = static_cast<int64_t>(E) * per_e;
+  // Dense: uniform token splits, enough waves for 256 CUs with at least 256
+  // tokens each.  Routed: an expert whose list holds more than `target` entries
+  // is cut into ceil(len / target) splits, target sized for ~2,048 workgroups
+  // over the launch (256 .. 1,024 entries), so the busiest expert's lists do not
+  // run as one serial chain; the cut experts' partials stay within 512 MiB.
+  int64_t nsplit = 1, split_len = T, target = 0, smax = 0, pmax = 0, hmax = 0;
   if (!ids) {
+    if (ntiles < 2048) {
+      nsplit = (2048 + ntiles - 1) / ntiles;
+      const int64_t by_tokens = (T + 255) / 256;
+      if (nsplit > by_tokens) nsplit = by_tokens;
+      if (nsplit < 1) nsplit = 1;
+    }
     split_len = ((T + nsplit - 1) / nsplit + kHTok - 1) / kHTok * kHTok;
     nsplit = (T + split_len - 1) / split_len;
+  } else {
+    const int64_t total = T * top_k;
+    target = (total * nb * 10 + 2047) / 2048;
+    target = target < 256 ? 256 : (target > 1024 ? 1024 : target);
+    target = (target + kHTok - 1) / kHTok * kHTok;
+    auto ceil_div = [](int64_t a, int64_t d) { return (a + d - 1) / d; };
+    // partial slots: only cut experts hold them, fewer than 2 total / target
+    pmax = 2 * ceil_div(total, target);
+    while (pmax > 2 && pmax * per_e * static_cast<int64_t>(sizeof(float)) > (int64_t(512) << 20)) {
+      target *= 2;
+      pmax = 2 * ceil_div(total, target);
+    }
+    smax = E + ceil_div(total, target);  // sum over experts of max(1, ceil(len / target))
+    hmax = ceil_div(total, target);      // cut experts: each holds more than target entries
+    if (hmax > E) hmax = E;
   }
-  const int64_t hn = static_cast<int64_t>(E) * (K / 256) * 65536;
-  // scratch: split partials; routed: bitmaps, repeat flags, list lengths and starts, lists
-  const size_t pbytes = nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0;
+  // scratch: split partials; routed: bitmaps, repeat flags, list lengths and
+  // starts (entries, split slots, partial slots), the cut experts, lists
+  const size_t pbytes = ids ? static_cast<size_t>(pmax) * per_e * sizeof(float)
+                            : (nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0);
   const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
   const size_t dbytes = ids ? static_cast<size_t>(T) : 0;
-  const size_t nbytes = ids ? static_cast<size_t>(2 * E + 1) * sizeof(int64_t) : 0;
+  const size_t nbytes = ids ? static_cast<size_t>(4 * E + 3) * sizeof(int64_t) + (E + 1) * sizeof(int32_t) : 0;
   const size_t lbytes = ids ? static_cast<size_t>(T) * top_k * sizeof(uint32_t) : 0;
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   const size_t off_b = up(pbytes), off_d = off_b + up(bbytes), off_n = off_d + up(dbytes), off_l = off_n + up(nbytes);
@@ -853,6 +950,9 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
   uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(base + off_d) : nullptr;
   int64_t *lens = ids ? reinterpret_cast<int64_t *>(base + off_n) : nullptr;
   int64_t *lstart = ids ? lens + E : nullptr;
+  int64_t *sstart = ids ? lstart + (E + 1) : nullptr;
+  int64_t *pstart = ids ? sstart + (E + 1) : nullptr;
+  int32_t *heavy = ids ? reinterpret_cast<int32_t *>(pstart + (E + 1)) : nullptr;
   uint32_t *list = ids ? reinterpret_cast<uint32_t *>(base + off_l) : nullptr;
   if (ids) {
     hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
@@ -860,23 +960,28 @@ int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t
     hipLaunchKernelGGL(route_count_kernel, dim3(static_cast<unsigned>((E + 3) / 4)), dim3(256), 0, stream,
                        static_cast<const uint32_t *>(bm), nchunks, E, W, lens);
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, static_cast<const int64_t *>(lens), E,
-                       lstart);
+                       target, lstart, sstart, pstart, heavy);
     hipLaunchKernelGGL(route_list_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream,
                        static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), nchunks, E, W,
                        chunk_rows, static_cast<const int64_t *>(lstart), list);
   }
-  float *dst = nsplit > 1 ? partial : hess;
-  const bool accumulate = nsplit == 1;
-  const dim3 g(static_cast<unsigned>(ntiles * nsplit));
+  const dim3 g(static_cast<unsigned>(ids ? smax * nb * 10 : ntiles * nsplit));
   if (dtype == 1)
     hipLaunchKernelGGL(hessian_kernel<1>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E,
-                       static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart), nsplit, split_len,
-                       dst, accumulate, status);
+                       static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart),
+                       static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart), nsplit, split_len,
+                       hess, partial, status);
   else
     hipLaunchKernelGGL(hessian_kernel<0>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E,
-                       static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart), nsplit, split_len,
-                       dst, accumulate, status);
-  if (nsplit > 1)
+                       static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart),
+                       static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart), nsplit, split_len,
+                       hess, partial, status);
+  if (ids)
+    hipLaunchKernelGGL(hessian_combine_routed_kernel, dim3(static_cast<unsigned>(hmax * ((per_e + 255) / 256))),
+                       dim3(256), 0, stream, static_cast<const float *>(partial),
+                       static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart),
+                       static_cast<const int32_t *>(heavy), E, per_e, hess);
+  else if (nsplit > 1)
     hipLaunchKernelGGL(hessian_combine_kernel, dim3(static_cast<unsigned>((hn + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float *>(partial), nsplit, hn, hess);
   const hipError_t le = hipGetLastError();

@@ -223,10 +223,12 @@ int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t co
  *           hess[e][b][i][j] += sum over the (t, s) pairs with ids[t][s] == e of
  *           x[t][256b + i] * x[t][256b + j] (dense: every token, e = 0).  Each
  *           block is exactly symmetric.  Tokens are added in ascending order
- *           (a token naming e twice, twice in a row) in fixed splits -- token
- *           ranges for a dense input, equal shares of each expert's routed
- *           tokens otherwise -- whose partial blocks are added in split order,
- *           so results repeat bit for bit.
+ *           (a token naming e twice, twice in a row) in fixed splits: token
+ *           ranges for a dense input; for routed input, an expert's list is cut
+ *           into equal shares only when it holds more entries than a length set
+ *           by T, top_k and K (256 to 1,024 entries, more if the partial blocks
+ *           would pass 512 MiB), else taken whole.  Partial blocks are added in
+ *           split order, so results repeat bit for bit.
  *  status   (device, nullable): IQ_STATUS_NONFINITE when a token that reached an
  *           expert holds a non-finite value; IQ_STATUS_BADID as
  *           iq_imatrix_collect.
