@@ -841,24 +841,31 @@ __global__ void __launch_bounds__(64) hessian_kernel(const void *__restrict__ x,
     nt = nn;
   }
   if (!finite) raise_status(status, ST_NONFINITE);
+  // Per 32 x 32 product: its 16 values and their mirror images (off-diagonal
+  // tiles) are read together, then added and written, so the read latency is
+  // paid once per product rather than once per value.
   float *Hb = Hdst;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
+    for (int n = 0; n < 2; ++n) {
+      const bool mirror = ti != tj;
+      const int col = tj * 64 + n * 32 + (lane & 31);
+      float od[16], om[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = ti * 64 + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int col = tj * 64 + n * 32 + (lane & 31);
-        const float v = acc[m][n][q];
-        if (accumulate) {
-          Hb[row * 256 + col] += v;
-          if (ti != tj) Hb[col * 256 + row] += v;
-        } else {
-          Hb[row * 256 + col] = v;
-          if (ti != tj) Hb[col * 256 + row] = v;
-        }
+        od[q] = accumulate ? Hb[row * 256 + col] : 0.0f;
+        om[q] = accumulate && mirror ? Hb[col * 256 + row] : 0.0f;
       }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = ti * 64 + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const float v = acc[m][n][q];
+        Hb[row * 256 + col] = accumulate ? od[q] + v : v;
+        if (mirror) Hb[col * 256 + row] = accumulate ? om[q] + v : v;
+      }
+    }
 }
 
 // hess[i] += partial[0][i] + partial[1][i] + ... in split order.
