@@ -1090,18 +1090,20 @@ __device__ __forceinline__ void unit_hdw_mfma(const float ha[UV], const float dw
 // The damped block is H + lambda I, lambda = perc_damp * mean(diag H).
 //
 // One workgroup per (expert, 64-row tile, block) with one wave per unit:
-// lanes are rows, so every H_ij is a wave-uniform operand shared by the 64
-// rows; wave v keeps its unit's weights and current residual in registers.
-// The every-choice sweep hands over each group's fields under every choice as
-// one word per (choice, group, row), rows contiguous, so the residuals come
-// from coalesced loads rather than from packed bytes.  Step A: wave v scores
-// every choice of unit v on the matrix cores (unit_hdw_mfma); the own-block
-// errors do not change between passes, so each wave keeps those of the choices
-// it scores later.  A revisit of unit u: every
-// other wave v forms its part H_uv dw_v on the matrix cores (unit_part_mfma: the
-// same fmaf chain); the waves add the parts in unit order
-// (each a slice of the rows of r); the waves score unit u's choices between
-// them, with u's weights passed through LDS; wave u takes the first minimum.
+// lanes are rows, H is shared by the 64 rows, and wave v keeps its unit's
+// weights and current residual in registers.  The products with H run on the
+// matrix cores as [UV x UV] . [UV x 64 rows] MFMA chains (one column per step,
+// so each is the fmaf chain above bit for bit), H's rows as the A operand and
+// the lanes' residuals as B.  The every-choice sweep hands over each group's
+// fields under every choice as one word per (choice, group, row), rows
+// contiguous, so the residuals come from coalesced loads rather than from
+// packed bytes.  Step A: wave v scores every choice of unit v
+// (unit_hdw_mfma); the own-block errors do not change between passes, so each
+// wave keeps those of the choices it scores later.  A revisit of unit u: every
+// other wave v forms its part H_uv dw_v (unit_part_mfma); the waves add the
+// parts in unit order (each a slice of the rows of r); the waves score unit
+// u's choices between them, with u's weights passed through LDS; wave u takes
+// the first minimum.
 // With A.out set, the workgroup then packs its block's payload under the
 // picks from the same field records (the every-choice sweep's fields under
 // choice c are the fixed-choice encoder's fields under c).
