@@ -54,8 +54,8 @@ def lib():
         L.orc_importance.argtypes = [P, P, ci, i64, ctypes.c_float, P]
         L.orc_merge.argtypes = [P, P, ci, i64, P, P]
         L.orc_hessian_collect.argtypes = [P, i64, i64, P, ci, ci, P]
-        L.orc_fixed_mean.argtypes = [P, i64]
-        L.orc_fixed_mean.restype = ctypes.c_float
+        L.orc_mean.argtypes = [P, i64]
+        L.orc_mean.restype = ctypes.c_float
         L.orc_anchor.argtypes = [ci, P, P]
         L.orc_anchor.restype = ctypes.c_uint16
         L.orc_encode_block.argtypes = [ci, P, P, P, ci, P, ci, P]
@@ -152,9 +152,10 @@ def importance(sums32, counts, floor_rel: float = 1e-6):
     return out, st
 
 
-def fixed_mean(m):
+def mean(m):
+    """The floor's mean of the m_j (fp32 result)."""
     m = _f32(m).ravel()
-    return float(lib().orc_fixed_mean(_p(m), m.size))
+    return float(lib().orc_mean(_p(m), m.size))
 
 
 def anchor(fmt, block):

@@ -36,8 +36,9 @@
  *  R5  amax == 0, fp16(d) == 0, non-finite inputs, fp16 overflow and
  *      out-of-range fixed choices give an all-zero block (the all-zero rule of
  *      the [3157] review); the last three also raise a status bit.
- *  R6  imatrix floor: a_j = sqrt(max(E_j, 1e-6 * mean_j E_j)); the mean is an
- *      exact fixed-point sum (orc_fixed_mean) so every summation order agrees.
+ *  R6  imatrix floor: a_j = sqrt(max(E_j, 1e-6 * mean_j E_j)); the mean is the
+ *      plain one: the E_j summed in fp64 in ascending j, divided by K in fp64,
+ *      rounded to fp32 (orc_mean).
  *  R7  odd sign parity (IQ2_XXS, IQ2_XS): per candidate entry, flip the element
  *      with the least a_j*|x_j|*g_kj (lowest j on ties).
  *  R8  x = -0 counts as positive.
@@ -212,27 +213,13 @@ int orc_hessian_collect(const float *x, int64_t T, int64_t K, const int32_t *ids
  * does", "Why the square root", "Shared floor"; [coverage] Facts: count 0 ->
  * weight 1 on every channel).  sums are the fp32 statistics.  R6.
  *
- * The floor is floor_rel times the mean of the m_j.  So that any summation
- * order gives the same bits, the mean is defined through an exact fixed-point
- * sum: with M = max_j m_j = f * 2^e (f in [0.5, 1)) and L = ceil(log2 K),
- * s = 62 - e - L, total = sum_j floor(m_j * 2^s) (an exact integer below 2^62),
- * mean = fp32( fp64(total) * 2^-s / K ). */
-static int ceil_log2(int64_t K) {
-  int L = 0;
-  while (((int64_t)1 << L) < K) ++L;
-  return L;
-}
-
-float orc_fixed_mean(const float *m, int64_t K) {
-  float M = 0.0f;
-  for (int64_t j = 0; j < K; ++j) M = fmaxf(M, m[j]);
-  if (M == 0.0f) return 0.0f;
-  int e;
-  frexp((double)M, &e);
-  int s = 62 - e - ceil_log2(K);
-  uint64_t total = 0;
-  for (int64_t j = 0; j < K; ++j) total += (uint64_t)floor(ldexp((double)m[j], s));
-  return (float)(ldexp((double)total, -s) / (double)K);
+ * The floor is floor_rel times the mean of the m_j, taken as the plain mean:
+ * the m_j added one after another in fp64, j ascending from 0, the total
+ * divided by K in fp64 and rounded to fp32. */
+float orc_mean(const float *m, int64_t K) {
+  double acc = 0.0;
+  for (int64_t j = 0; j < K; ++j) acc += (double)m[j];
+  return (float)(acc / (double)K);
 }
 
 int orc_importance(const float *sums, const int64_t *counts, int num_experts, int64_t K,
@@ -250,7 +237,7 @@ int orc_importance(const float *sums, const int64_t *counts, int num_experts, in
         if (!isfinite(m[j]) || m[j] < 0.0f) { st |= ORC_ST_BADIMP; flat = 1; }
       }
     }
-    float mean = flat ? 0.0f : orc_fixed_mean(m, K);
+    float mean = flat ? 0.0f : orc_mean(m, K);
     if (flat || mean == 0.0f) { /* idle expert or nothing usable: flat weights */
       for (int64_t j = 0; j < K; ++j) ie[j] = 1.0f;
       continue;

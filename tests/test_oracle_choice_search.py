@@ -9,6 +9,10 @@
   the others fixed (fp64 check, margin-aware).
 * On correlated inputs the Hessian picks lower the layer-output error against
   the imatrix picks (the PR's own test, as a sum over blocks).
+* The damping (R16: perc_damp times the mean of the block's diagonal, as GPTQ
+  damps) equals numpy's evaluation of that definition, and under a
+  block-diagonal Hessian, where every unit is independent, the damped picks are
+  the fp64 minimisers of dw (H + lambda I) dw^T wherever the margin is clear.
 """
 import numpy as np
 import pytest
@@ -41,6 +45,14 @@ def decoded_dw(orc, fmt, w, grid, imp, choices):
 def block_error(dw, H, lam):
     Hd = H.astype(np.float64) + lam * np.eye(256)
     return float(dw @ Hd @ dw)
+
+
+def numpy_damping(H, perc_damp):
+    """R16 evaluated with numpy: the diagonal added in fp64 in ascending order
+    (cumsum is a sequential scan), divided by 256, rounded to fp32, times
+    perc_damp in fp32."""
+    diag = np.diag(np.asarray(H, np.float32)).astype(np.float64)
+    return np.float32(np.float32(perc_damp) * np.float32(np.cumsum(diag)[-1] / 256.0))
 
 
 def lattice_rows(seed, rows):
@@ -123,7 +135,7 @@ def test_passes_never_raise_block_error_and_last_unit_is_optimal(orc, fmt):
     every = [decoded_dw(orc, fmt, w, grid, imp, np.full(picks.shape, c, np.uint8)) for c in range(NC)]
     for r in range(w.shape[0]):
         for b in range(2):
-            lam = orc.damping(H[0, b], 0.3)
+            lam = float(numpy_damping(H[0, b], 0.3))
             Hd = H[0, b].astype(np.float64) + lam * np.eye(256)
             sl = slice(256 * b, 256 * b + 256)
             own = np.zeros(U, int)
@@ -163,3 +175,77 @@ def test_hessian_picks_lower_output_error_on_correlated_inputs(orc):
             e_lh += block_error(dw_lh[r, sl], H[0, b], 0.0)
             e_im += block_error(dw_im[r, sl], H[0, b], 0.0)
     assert e_lh < e_im
+
+
+def test_damping_is_perc_damp_times_mean_diagonal(orc):
+    g = inputs.rng(3400)
+    for _ in range(20):
+        H = g.standard_normal((256, 256)).astype(np.float32)
+        H[np.arange(256), np.arange(256)] = g.lognormal(0, 4, 256).astype(np.float32)
+        H[1:, 0] = np.float32(1e6)   # a first column a wrong stride would read
+        H[0, 1:] = np.float32(-1e6)  # and a first row
+        for p in (0.0, 0.3, 0.01, 1.0):
+            lam = orc.damping(H, p)
+            assert lam == numpy_damping(H, p)
+            if p:
+                diag = np.diag(H).astype(np.float64)
+                assert lam != np.float32(p) * np.float32(diag.max())
+                assert abs(lam - p * diag.mean()) <= 1e-6 * p * diag.mean()
+
+
+def _unit_hessians(g, U, UV):
+    """A block-diagonal 256x256 H: unit u's block Q diag(ev) Q^T with eigenvalues
+    spread over five decades, so adding lambda I reorders the choices."""
+    H = np.zeros((256, 256), np.float64)
+    for u in range(U):
+        q, _ = np.linalg.qr(g.standard_normal((UV, UV)))
+        ev = np.logspace(-3, 2, UV) * g.lognormal(0, 1)
+        H[u * UV:(u + 1) * UV, u * UV:(u + 1) * UV] = (q * ev) @ q.T
+    H = (H + H.T) / 2
+    return H.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_damped_picks_are_fp64_minimisers_under_block_diagonal_h(orc, fmt):
+    g = inputs.rng(3500 + FORMATS.index(fmt))
+    geo = orc.geometry(fmt)
+    U, UV, NC = geo["units"], 8 * geo["groups_per_unit"], geo["num_choices"]
+    rows = 12
+    w = inputs.weight(rows, 256, 3510, 3511, bf16=False)
+    grid = inputs.grid_for(fmt, 3512)
+    imp = inputs.importance_like(256, 3513)[None, :]
+    H = _unit_hessians(g, U, UV)
+    every = [decoded_dw(orc, fmt, w, grid, imp, np.full((rows, 1, U), c, np.uint8)) for c in range(NC)]
+    diag = np.diag(H).astype(np.float64)
+
+    def fp64_picks(lam):
+        """argmin over choices of dw (H_uu + lam I) dw per (row, unit), and
+        whether the best beats the runner-up by a clear margin."""
+        picks = np.zeros((rows, U), int)
+        clear = np.zeros((rows, U), bool)
+        for u in range(U):
+            cols = slice(u * UV, (u + 1) * UV)
+            Hd = H[cols, cols].astype(np.float64) + lam * np.eye(UV)
+            errs = np.stack([np.einsum("ri,ij,rj->r", every[c][:, cols], Hd, every[c][:, cols]) for c in range(NC)])
+            order = np.sort(errs, axis=0)
+            picks[:, u] = np.argmin(errs, axis=0)
+            clear[:, u] = (order[1] - order[0]) > 1e-5 * np.abs(order[0]) + 1e-12
+        return picks, clear
+
+    seen_change = 0
+    for p in (0.0, 0.3):
+        got, st = orc.choice_search(fmt, w, grid, H[None, None], imp, perc_damp=p)
+        assert st == 0
+        got = got[:, 0, :]
+        want, clear = fp64_picks(p * diag.mean())
+        assert clear.mean() > 0.9
+        assert np.array_equal(got[clear], want[clear])
+        if p:
+            undamped, clear0 = fp64_picks(0.0)
+            both = clear & clear0
+            seen_change = int((undamped[both] != want[both]).sum())
+            # a wrong lambda (the largest diagonal entry instead of the mean)
+            # would pick differently somewhere
+            wrong, clear_w = fp64_picks(p * diag.max())
+            assert (wrong[clear & clear_w] != got[clear & clear_w]).any()
+    assert seen_change > 0

@@ -244,20 +244,11 @@ def test_collect_flags_nonfinite_and_bad_ids(orc):
 # --------------------------------------------------------------------------
 # Importance: closed form of the floored square root, flat for idle experts
 # --------------------------------------------------------------------------
-def _exact_fixed_mean(m):
-    """The floor's mean from its definition, in Python integers."""
-    from fractions import Fraction
-    import math
-    m = np.asarray(m, np.float32)
-    M = float(m.max())
-    if M == 0:
-        return 0.0
-    e = math.frexp(M)[1]
-    L = max(0, math.ceil(math.log2(m.size)))
-    s = 62 - e - L
-    total = sum(math.floor(Fraction(float(v)) * Fraction(2) ** s) for v in m)
-    assert total < 2 ** 62
-    return float(np.float32(float(total) * 2.0 ** -s / m.size))
+def _sequential_mean(m):
+    """The plain mean as numpy evaluates it: a running fp64 sum (cumsum is a
+    sequential scan, unlike sum's pairwise tree), divided by K, rounded to fp32."""
+    m = np.asarray(m, np.float32).astype(np.float64)
+    return np.float32(np.cumsum(m)[-1] / m.size)
 
 
 def test_importance_closed_form(orc):
@@ -271,15 +262,13 @@ def test_importance_closed_form(orc):
     assert np.all(imp[1] == 1.0)           # count 0 -> weight 1 on every channel
     for e in (0, 2, 3):
         m = (sums[e] / np.float32(counts[e])).astype(np.float32)
-        mean = _exact_fixed_mean(m)
-        assert orc.fixed_mean(m) == np.float32(mean)
-        # the fixed-point mean is the true mean to fp64 accuracy
-        assert abs(mean - m.astype(np.float64).mean()) <= 1e-6 * mean
-        fl = np.float32(np.float32(1e-6) * np.float32(mean))
+        mean = _sequential_mean(m)
+        assert orc.mean(m) == mean
+        fl = np.float32(np.float32(1e-6) * mean)
         ref = np.sqrt(np.maximum(m, fl)).astype(np.float32)
         assert np.array_equal(imp[e], ref)
-    assert np.all(imp[2, :7] == np.sqrt(np.float32(np.float32(1e-6) * np.float32(
-        _exact_fixed_mean((sums[2] / np.float32(37)).astype(np.float32))))))
+    assert np.all(imp[2, :7] == np.sqrt(np.float32(np.float32(1e-6) * _sequential_mean(
+        (sums[2] / np.float32(37)).astype(np.float32)))))
     # all-zero statistic with count > 0: nothing usable -> flat
     imp2, _ = orc.importance(np.zeros((1, 8), np.float32), np.array([5]), 1e-6)
     assert np.all(imp2 == 1.0)
@@ -290,13 +279,26 @@ def test_importance_closed_form(orc):
     assert st3 & orc.ST_BADIMP and np.all(imp3 == 1.0)
 
 
-def test_fixed_mean_order_free_and_exact(orc):
+def test_mean_is_the_sequential_fp64_mean(orc):
+    """R6's mean against numpy's sequential fp64 scan on wide-range data, and
+    two hand cases whose fp32 result tells the readings apart."""
     g = inputs.rng(19)
-    for K in (1, 7, 2048, 5000):
-        m = (g.lognormal(0, 3, K)).astype(np.float32)
+    for K in (1, 7, 2048, 5000, 17408):
+        m = (g.lognormal(0, 6, K)).astype(np.float32)
         m[g.random(K) < 0.1] = 0.0
-        assert orc.fixed_mean(m) == np.float32(_exact_fixed_mean(m))
-        assert orc.fixed_mean(g.permutation(m)) == orc.fixed_mean(m)
+        assert orc.mean(m) == _sequential_mean(m)
+    # a case that separates the readings: the running fp64 sum keeps
+    # 4 + 2^-22 and drops each 2^-52 (below half an ulp of ~4), so the mean is
+    # 0.5 + 2^-25, the midpoint between two fp32 values, which rounds to even
+    # (0.5); the exact total, or numpy's pairwise sum, lies above it and rounds
+    # up to 0.5 + 2^-24
+    m = np.array([4.0, 2.0 ** -22] + [2.0 ** -52] * 6, np.float32)
+    assert orc.mean(m) == _sequential_mean(m) == np.float32(0.5)
+    from fractions import Fraction
+    up = np.float32(0.5 + 2.0 ** -24)
+    assert np.float32(m.astype(np.float64).sum() / 8) == up
+    exact = sum(Fraction(float(v)) for v in m) / 8
+    assert float(exact) > 0.5 + 2.0 ** -25 and np.float32(float(exact)) == up
 
 
 # --------------------------------------------------------------------------
