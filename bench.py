@@ -9,10 +9,24 @@ before the timed region.  `value` = encoded elements per second of the whole
 step (M elem/s).
 
 Also reported: the dominant kernel's roofline (the encoder's search kernel,
-timed alone with HIP events around its own launches), per-layout encode
-throughput on the same weight, the fixed-choice IQ2_S variant, the IQ1 layouts
-on 17408x5120, the fused-MoE workload, and the CPU oracle's throughput on a
-bounded sample of the same step.
+timed alone with HIP events around its own launches) in FLOP against the fp32
+vector peak and against the measured ceiling of its instruction mix, per-layout
+encode throughput on the same weight, the fixed-choice IQ2_S variant, the IQ1
+layouts on 17408x5120, the fused-MoE workload, and the CPU oracle's throughput
+on a bounded sample of the same step.
+
+Work model (FLOP, an FMA two, a MUL, ADD or MIN one), what the exhaustive
+search needs and no more:
+  per (row, 8-value group, grid entry): the -2P chain (8 FMA, 16) and the 16
+    candidates of that entry (one FMA and one MIN each, 48); IQ1 adds the two
+    shift terms (2 FMA, 4); an IQ2_XXS / IQ2_XS group with an odd count of
+    negative values adds the parity term (8 MUL, 7 MIN, 1 FMA: 17), an even
+    one needs none;
+  per (expert, 8-column group, grid entry): the weighted norm (IQ2: 8 MUL and
+    8 FMA, 24; IQ1: per shift 8 ADD, 8 MUL, 8 FMA, 64), which does not depend
+    on the row.
+The per-group setup (a few ops per value), the unit scoring (a few ops per
+choice per group) and the index recovery of the argmin are not counted.
 """
 from __future__ import annotations
 
@@ -27,15 +41,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "encode M elem/s per IQ format on 5632×2048 (+ % of compute roofline)"
-# Algorithmic work of the exhaustive search per weight element (FMA, MUL and MIN
-# count one op each): per (group, entry) the grid terms (IQ2_S 16, parity
-# layouts and IQ1 32) plus 2 ops for each of the 16 (choice or shift, scale)
-# candidates, times entries / 8 elements per group.
-OPS_PER_ELEM = {"IQ2_XXS": 2048, "IQ2_XS": 4096, "IQ2_S": 6144, "IQ1_S": 16384, "IQ1_M": 16384}
-# VALU peak: 256 CUs x 64 lanes x 2 ops per lane per clock (a 3-input min or a
-# packed FMA retires two) x 2.4 GHz
-PEAK_TOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+GRID_N = {"IQ2_XXS": 256, "IQ2_XS": 512, "IQ2_S": 1024, "IQ1_S": 2048, "IQ1_M": 2048}
+# FLOP per (row, group, entry) for every group, and extra for odd-parity groups
+ENTRY_FLOP = {"IQ2_XXS": (64, 17), "IQ2_XS": (64, 17), "IQ2_S": (64, 0), "IQ1_S": (68, 0), "IQ1_M": (68, 0)}
+# FLOP per (expert, column group, entry): the weighted norms
+NORM_FLOP = {"IQ2_XXS": 24, "IQ2_XS": 24, "IQ2_S": 24, "IQ1_S": 64, "IQ1_M": 64}
+# MI355X fp32 vector peak (AMD's published dense figure): 157.3 TFLOP/s
+PEAK_TFLOPS = 157.3
 GRID_SEED = {"IQ2_XXS": 201, "IQ2_XS": 202, "IQ2_S": 203, "IQ1_S": 204, "IQ1_M": 204}
+
+
+def search_flop(fmt: str, rows: int, cols: int, experts: int, odd_groups: int) -> int:
+    """FLOP the exhaustive search of one encode needs (module docstring)."""
+    n = GRID_N[fmt]
+    base, parity = ENTRY_FLOP[fmt]
+    groups = rows * cols // 8
+    return n * (groups * base + odd_groups * parity) + n * experts * (cols // 8) * NORM_FLOP[fmt]
+
+
+def odd_parity_groups(w) -> int:
+    """8-value groups of w with an odd count of negative values (-0 counts as
+    positive), which are the groups the parity layouts charge a flip."""
+    import torch
+    neg = (w.view(w.shape[0], -1, 8) < 0).sum(dim=-1)
+    return int((neg % 2).sum().item())
 
 
 def source_hash() -> str:
@@ -61,20 +90,30 @@ def cpu_model() -> str | None:
     return None
 
 
-def measured_valu_peak(iters: int = 2000) -> dict:
-    """What this GPU sustains for the sweep's instruction forms (independent
-    chains, 8 waves per SIMD, built like the encoder): VGPR-only fp32 FMA, the
-    3-input min, and the candidate mix of two FMAs per 3-input min; in
-    algorithmic ops (FMA 1, 3-input min 2), with the shader clock measured
-    during the run.  From libvalu_peak.so (ggml_iq_codebook_imatrix_amd/peak)."""
+def _peak_lib():
     import ctypes
     path = os.path.join(ROOT, "ggml_iq_codebook_imatrix_amd", "libvalu_peak.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: run the package build first")
     L = ctypes.CDLL(path)
-    d = ctypes.c_double
-    L.valu_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(d), ctypes.POINTER(d), ctypes.POINTER(d)]
+    d = ctypes.POINTER(ctypes.c_double)
+    L.valu_peak.argtypes = [ctypes.c_int, ctypes.c_int, d, d, d]
     L.valu_peak.restype = ctypes.c_int
+    L.shader_clock.argtypes = [ctypes.c_int, d]
+    L.shader_clock.restype = ctypes.c_int
+    return L
+
+
+def measured_valu_peak(iters: int = 2000) -> dict:
+    """What this GPU sustains for the sweep's instruction forms (independent
+    chains, 8 waves per SIMD, built like the encoder): VGPR-only fp32 FMA, the
+    3-input min, and the candidate mix of two FMAs per 3-input min; in
+    algorithmic ops (FMA 1, 3-input min 2) and, for the mix, in FLOP (two FMAs
+    and two MINs: 6 FLOP per 4 ops), with the shader clock measured during the
+    run.  From libvalu_peak.so (ggml_iq_codebook_imatrix_amd/peak)."""
+    import ctypes
+    L = _peak_lib()
+    d = ctypes.c_double
     out = {}
     clocks = []
     for mode, name in ((0, "fma"), (1, "min3"), (2, "mix")):
@@ -84,8 +123,24 @@ def measured_valu_peak(iters: int = 2000) -> dict:
         out[f"{name}_TOP_s"] = round(ops.value / 1e12, 2)
         out[f"{name}_Tinstr_s"] = round(ins.value / 1e12, 2)
         clocks.append(clk.value)
+    out["mix_TFLOP_s"] = round(out["mix_TOP_s"] * 1.5, 2)
     out["clock_GHz"] = round(min(clocks) / 1e9, 3) if min(clocks) > 0 else None
     return out
+
+
+def shader_clock_ghz(us: int = 200) -> float | None:
+    import ctypes
+    c = ctypes.c_double()
+    return round(c.value / 1e9, 3) if _peak_lib().shader_clock(us, ctypes.byref(c)) == 0 else None
+
+
+def frac(achieved: float, peak: float, what: str) -> float:
+    """achieved / peak; above 1 the work model counts work the kernel does not
+    do, so the figure is refused rather than printed."""
+    f = achieved / peak
+    if f > 1.0:
+        raise RuntimeError(f"{what}: {achieved:.2f} of a {peak:.2f} peak -- the work model is wrong")
+    return round(f, 4)
 
 
 def main() -> int:
@@ -141,7 +196,10 @@ def main() -> int:
     packed = torch.empty((rows, cols // 256, api.format_info(fmt)["block_bytes"]), dtype=torch.uint8, device=dev)
     w_hat = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
     status = api.new_status(dev)
-    log("inputs ready", fmt, rows, cols, "tokens", T)
+    ws_c = torch.empty(api.collect_workspace_size(T, cols), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(api.quantize_workspace_size(fmt, rows, cols), dtype=torch.uint8, device=dev)
+    odd = odd_parity_groups(w)
+    log("inputs ready", fmt, rows, cols, "tokens", T, "odd-parity groups", odd)
 
     ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -149,13 +207,16 @@ def main() -> int:
     def step(i=None):
         sums.zero_()
         counts.zero_()
-        api.imatrix_collect(x, chunk_rows=1024, sums=sums, counts=counts, status=status)
+        api.imatrix_collect(x, chunk_rows=1024, sums=sums, counts=counts, status=status, workspace=ws_c)
         api.imatrix_importance(sums, counts, out=imp, status=status)
-        if i is not None:
-            api.time_next_search(ev_s[i], ev_e[i])
-        api.quantize(fmt, w, grid, imp, out=packed, status=status)
+        api.quantize(fmt, w, grid, imp, out=packed, status=status, workspace=ws_q,
+                     events=None if i is None else (ev_s[i], ev_e[i]))
         api.dequantize(fmt, packed, grid, out=w_hat)
 
+    # the measured ceilings run first: they also bring the clocks up before the
+    # untimed warm-up steps
+    meas = measured_valu_peak()
+    log("measured VALU ceiling", meas)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -168,13 +229,14 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock_after = shader_clock_ghz()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     search_ms = float(np.mean([ev_s[i].elapsed_time(ev_e[i]) for i in range(args.steps)]))
     value = rows * cols / (ms_per_step * 1e-3) / 1e6
-    log(f"step {ms_per_step:.4f} ms, search kernel {search_ms:.4f} ms")
+    log(f"step {ms_per_step:.4f} ms, search kernel {search_ms:.4f} ms, clock after {clock_after} GHz")
 
-    ops = OPS_PER_ELEM[fmt] * rows * cols
-    achieved = ops / (search_ms * 1e-3) / 1e12
+    flop = search_flop(fmt, rows, cols, 1, odd)
+    achieved = flop / (search_ms * 1e-3) / 1e12
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "search_iq2_xs_5632x2048_traffic.json")
     if os.path.exists(tpath):
@@ -182,28 +244,32 @@ def main() -> int:
             tr = json.load(f)
         if tr.get("source_hash") == source_hash():
             traffic = tr.get("bytes_per_launch")
-    roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_TOPS, 2), "unit": "TOP/s",
-                "frac": round(achieved / PEAK_TOPS, 4), "traffic": traffic,
-                "kernel": "search_kernel<IQ2_XS>", "ops_per_launch": ops, "ms_per_launch": round(search_ms, 4)}
-    meas = measured_valu_peak()
-    meas["frac_of_mix"] = round(achieved / meas["mix_TOP_s"], 4)
+    roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": frac(achieved, PEAK_TFLOPS, "search kernel vs fp32 peak"), "traffic": traffic,
+                "kernel": "search_kernel<IQ2_XS>", "flop_per_launch": flop,
+                "flop_per_elem": round(flop / (rows * cols), 1), "odd_parity_groups": odd,
+                "ms_per_launch": round(search_ms, 4),
+                "measured_mix_TFLOP_s": meas["mix_TFLOP_s"],
+                "frac_of_measured_mix": frac(achieved, meas["mix_TFLOP_s"], "search kernel vs measured mix"),
+                "clock_GHz_ceiling_run": meas["clock_GHz"], "clock_GHz_after_timed_steps": clock_after}
     roofline["measured"] = meas
-    log("measured VALU ceiling", meas)
 
     # ---------------- extras: every layout on the same weight --------------
     extras = {}
     if not args.no_extras:
-        def time_encode(f, wd, g, impd, rpe=None, choices=None, reps=args.reps):
-            out = api.quantize(f, wd, g, impd, rows_per_expert=rpe, choices=choices)
+        def time_encode(f, wd, g, impd, rpe=None, choices=None, reps=args.reps, odd_groups=None):
+            ws = torch.empty(api.quantize_workspace_size(f, wd.shape[0], wd.shape[1], rpe, impd is not None),
+                             dtype=torch.uint8, device=dev)
+            out = api.quantize(f, wd, g, impd, rows_per_expert=rpe, choices=choices, workspace=ws)
             torch.cuda.synchronize()
             es = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
             ee = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
             ks = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
             ke = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
             for r in range(reps):
-                api.time_next_search(ks[r], ke[r])
                 es[r].record()
-                api.quantize(f, wd, g, impd, rows_per_expert=rpe, choices=choices, out=out)
+                api.quantize(f, wd, g, impd, rows_per_expert=rpe, choices=choices, out=out, workspace=ws,
+                             events=(ks[r], ke[r]))
                 ee[r].record()
             torch.cuda.synchronize()
             whole = float(np.median([es[r].elapsed_time(ee[r]) for r in range(reps)]))
@@ -212,15 +278,19 @@ def main() -> int:
             res = {"encode_ms": round(whole, 4), "search_ms": round(kern, 4),
                    "encode_M_elem_s": round(n / whole / 1e3, 1)}
             if choices is None:
-                a = OPS_PER_ELEM[f] * n / (kern * 1e-3) / 1e12
-                res["search_TOP_s"] = round(a, 2)
-                res["roofline_frac"] = round(a / PEAK_TOPS, 4)
+                E = 1 if rpe is None else wd.shape[0] // rpe
+                if odd_groups is None:
+                    odd_groups = odd_parity_groups(wd)
+                a = search_flop(f, wd.shape[0], wd.shape[1], E, odd_groups) / (kern * 1e-3) / 1e12
+                res["search_TFLOP_s"] = round(a, 2)
+                res["roofline_frac"] = frac(a, PEAK_TFLOPS, f"{f} search vs fp32 peak")
+                res["frac_of_measured_mix"] = frac(a, meas["mix_TFLOP_s"], f"{f} search vs measured mix")
             return res
 
         per = {}
         for f in api.FORMATS:
             g = torch.from_numpy(inputs.grid_for(f, GRID_SEED[f])).to(dev)
-            per[f] = time_encode(f, w, g, imp)
+            per[f] = time_encode(f, w, g, imp, odd_groups=odd)
             log(f, per[f])
         g = torch.from_numpy(inputs.grid_for("IQ2_S", 203)).to(dev)
         ch = torch.full((rows, cols // 256, 16), 7, dtype=torch.uint8, device=dev)
@@ -342,7 +412,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        threads = min(os.cpu_count() or 1, 16)
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
         t = time.perf_counter()
         oracle.quantize(fmt, w32[:32], grid32, np.ones((1, cols), np.float32), threads=threads)
         per_row = (time.perf_counter() - t) / 32

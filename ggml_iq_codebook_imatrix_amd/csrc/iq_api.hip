@@ -1,5 +1,7 @@
 // iq_api.hip -- the C ABI of libiq.so (declared in include/iq.h): host-side
-// validation, then the launches.  No entry point synchronises the stream.
+// validation, workspace queries, then the launches.  No entry point allocates
+// device memory or synchronises the stream; every size a launch depends on is
+// checked before the first kernel is enqueued.
 
 #include "iq.h"
 #include "iq_common.hpp"
@@ -20,20 +22,110 @@ constexpr FmtRow kFmt[5] = {
     {56, 2048, 16, 8, 2},  // IQ1_M
 };
 
-thread_local hipEvent_t t_search_start = nullptr, t_search_stop = nullptr;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;  // workgroups in one grid dimension
 
 bool bad_fmt(int fmt) { return fmt < 0 || fmt > 4; }
 bool bad_dtype(int dt) { return dt != IQ_DTYPE_F32 && dt != IQ_DTYPE_BF16; }
+bool fits(int64_t wgs) { return wgs >= 0 && wgs <= kMaxGrid; }
+
+// Shape checks shared by the encoder entry points and their workspace queries.
+int check_encode_shape(int64_t rows, int64_t cols, int64_t rpe, int fmt, int64_t units_per_wg_col) {
+  if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
+  if (rpe < 1 || rows % rpe != 0) return IQ_ERR_SHAPE;
+  if (cols / 256 > (int64_t(1) << 24) || rows > (int64_t(1) << 40)) return IQ_ERR_SHAPE;
+  const int64_t E = rows / rpe, nb = cols / 256;
+  if (rows > (int64_t(1) << 40) / nb) return IQ_ERR_SHAPE;  // blocks: keeps the products below in range
+  // search workgroups: experts x 64-row tiles x column sets
+  if (!fits(E * ((rpe + 63) / 64) * nb * units_per_wg_col)) return IQ_ERR_SHAPE;
+  // norm-table, importance-check and anchor launches
+  const int64_t gblocks = (E * (cols / 8) * kFmt[fmt].grid_size + 255) / 256;
+  if (!fits(gblocks + (E * nb + 3) / 4) || !fits((rows * nb + 7) / 8)) return IQ_ERR_SHAPE;
+  return IQ_OK;
+}
+
+int64_t wg_cols(int fmt) { return 32 / (fmt == IQ_FMT_IQ1_M ? 8 : 4); }
+
+int check_workspace(size_t need, const void *ws, size_t ws_bytes) {
+  if (need == 0) return IQ_OK;
+  if (!ws) return IQ_ERR_NULL;
+  if (ws_bytes < need) return IQ_ERR_WORKSPACE;
+  return IQ_OK;
+}
+
+int check_collect_args(int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int num_experts,
+                       int chunk_rows) {
+  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
+  if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1) return IQ_ERR_ARG;
+  if (ids && top_k < 1) return IQ_ERR_ARG;
+  if (!ids && num_experts != 1 && T != 0) return IQ_ERR_ARG;  // no tokens: ids may be NULL
+  if (static_cast<int64_t>(num_experts) * K > (int64_t(1) << 40)) return IQ_ERR_ARG;
+  return IQ_OK;
+}
+
+int check_collect_grids(int64_t T, int64_t K, bool routed, int E, int chunk_rows) {
+  if (T == 0) return IQ_OK;
+  const iq::CollectPlan P = iq::plan_collect(T, K, routed, E, chunk_rows);
+  if (!fits(P.wchunks * P.nsub * E * P.ntile) || !fits((static_cast<int64_t>(E) * K + 255) / 256) ||
+      !fits(P.wchunks * ((chunk_rows + 255) / 256)))
+    return IQ_ERR_ARG;
+  return IQ_OK;
+}
+
+int check_hessian_args(int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int num_experts,
+                       int chunk_rows) {
+  const int rc = check_collect_args(dtype, T, K, ids, top_k, num_experts, chunk_rows);
+  if (rc != IQ_OK) return rc;
+  if (K % 256 != 0) return IQ_ERR_SHAPE;
+  if (static_cast<int64_t>(num_experts) * K > (int64_t(1) << 30) || T > (int64_t(1) << 31) - 1) return IQ_ERR_ARG;
+  if (T == 0) return IQ_OK;
+  const iq::HessPlan P = iq::plan_hessian(T, K, ids ? top_k : 0, num_experts, chunk_rows);
+  const int64_t nb = K / 256, per_e = nb * 65536;
+  if (ids) {
+    if (!fits(P.smax * nb * 10) || !fits(P.hmax * ((per_e + 255) / 256)) ||
+        !fits(P.nchunks * ((chunk_rows + 255) / 256)) || T * top_k > (int64_t(1) << 32))
+      return IQ_ERR_ARG;
+  } else if (!fits(num_experts * nb * 10 * P.nsplit)) {
+    return IQ_ERR_ARG;
+  }
+  return IQ_OK;
+}
+
+iq::EncArgs enc_args(const void *w, int dtype, int64_t rows, int64_t cols, int64_t rpe, const float *grid,
+                     const float *importance, int32_t *status) {
+  iq::EncArgs A{};
+  A.w = w;
+  A.dtype = dtype;
+  A.rows = rows;
+  A.cols = cols;
+  A.rpe = rpe;
+  A.E = rows / rpe;
+  A.nb = static_cast<int>(cols / 256);
+  A.grid = grid;
+  A.imp = importance;
+  A.status = status;
+  return A;
+}
+
+int quantize_common(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                    const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
+                    void *workspace, size_t workspace_bytes, int32_t *status, bool every, hipEvent_t ev0,
+                    hipEvent_t ev1, hipStream_t stream) {
+  if (bad_fmt(fmt)) return IQ_ERR_FMT;
+  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
+  if (!grid || (rows != 0 && (!w || !out))) return IQ_ERR_NULL;
+  int rc = check_encode_shape(rows, cols, rows_per_expert, fmt, wg_cols(fmt));
+  if (rc != IQ_OK) return rc;
+  const size_t need = rows ? iq::plan_quantize(fmt, rows, cols, rows_per_expert, importance != nullptr).bytes : 0;
+  if ((rc = check_workspace(need, workspace, workspace_bytes)) != IQ_OK) return rc;
+  iq::EncArgs A = enc_args(w, dtype, rows, cols, rows_per_expert, grid, importance, status);
+  A.choices = choices;
+  A.out = out;
+  A.copies = every ? kFmt[fmt].num_choices : 1;
+  A.copy_stride = rows * (cols / 256) * kFmt[fmt].block_bytes;
+  return iq::launch_quantize(fmt, A, every, workspace, ev0, ev1, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
+}
 
 }  // namespace
-
-namespace iq {
-void take_search_events(hipEvent_t *start, hipEvent_t *stop) {
-  *start = t_search_start;
-  *stop = t_search_stop;
-  t_search_start = t_search_stop = nullptr;
-}
-}  // namespace iq
 
 extern "C" {
 
@@ -49,31 +141,50 @@ int iq_format_info(int fmt, iq_format_info_t *out) {
   return IQ_OK;
 }
 
-int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
-                       int num_experts, int chunk_rows, float *sums, int64_t *counts, int32_t *status,
-                       hipStream_t stream) {
-  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!sums || !counts || (T != 0 && !x)) return IQ_ERR_NULL;
-  if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1) return IQ_ERR_ARG;
-  if (ids && top_k < 1) return IQ_ERR_ARG;
-  if (!ids && num_experts != 1 && T != 0) return IQ_ERR_ARG;  // no tokens: ids may be NULL
+int iq_imatrix_collect_workspace_size(int64_t T, int64_t K, int top_k, int num_experts, int chunk_rows,
+                                      size_t *bytes) {
+  if (!bytes) return IQ_ERR_NULL;
+  if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1 || top_k < 0) return IQ_ERR_ARG;
   if (static_cast<int64_t>(num_experts) * K > (int64_t(1) << 40)) return IQ_ERR_ARG;
+  *bytes = T ? iq::plan_collect(T, K, top_k > 0, num_experts, chunk_rows).bytes : 0;
+  return IQ_OK;
+}
+
+int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
+                       int num_experts, int chunk_rows, float *sums, int64_t *counts, void *workspace,
+                       size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+  int rc = check_collect_args(dtype, T, K, ids, top_k, num_experts, chunk_rows);
+  if (rc != IQ_OK) return rc;
+  if (!sums || !counts || (T != 0 && !x)) return IQ_ERR_NULL;
+  if ((rc = check_collect_grids(T, K, ids != nullptr, num_experts, chunk_rows)) != IQ_OK) return rc;
+  const size_t need = T ? iq::plan_collect(T, K, ids != nullptr, num_experts, chunk_rows).bytes : 0;
+  if ((rc = check_workspace(need, workspace, workspace_bytes)) != IQ_OK) return rc;
   return iq::launch_collect(x, dtype, T, K, ids, ids ? top_k : 0, num_experts, chunk_rows, sums, counts, status,
-                            stream) == 0
+                            workspace, stream) == 0
              ? IQ_OK
              : IQ_ERR_HIP;
 }
 
-int iq_hessian_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
-                       int num_experts, int chunk_rows, float *hess, int32_t *status, hipStream_t stream) {
-  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!hess || (T != 0 && !x)) return IQ_ERR_NULL;
-  if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1) return IQ_ERR_ARG;
-  if (ids && top_k < 1) return IQ_ERR_ARG;
-  if (!ids && num_experts != 1 && T != 0) return IQ_ERR_ARG;  // no tokens: ids may be NULL
+int iq_hessian_collect_workspace_size(int64_t T, int64_t K, int top_k, int num_experts, int chunk_rows,
+                                      size_t *bytes) {
+  if (!bytes) return IQ_ERR_NULL;
+  if (T < 0 || K <= 0 || num_experts < 1 || chunk_rows < 1 || top_k < 0) return IQ_ERR_ARG;
   if (K % 256 != 0) return IQ_ERR_SHAPE;
   if (static_cast<int64_t>(num_experts) * K > (int64_t(1) << 30) || T > (int64_t(1) << 31) - 1) return IQ_ERR_ARG;
-  return iq::launch_hessian(x, dtype, T, K, ids, ids ? top_k : 0, num_experts, chunk_rows, hess, status, stream) == 0
+  *bytes = T ? iq::plan_hessian(T, K, top_k, num_experts, chunk_rows).bytes : 0;
+  return IQ_OK;
+}
+
+int iq_hessian_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
+                       int num_experts, int chunk_rows, float *hess, void *workspace, size_t workspace_bytes,
+                       int32_t *status, hipStream_t stream) {
+  int rc = check_hessian_args(dtype, T, K, ids, top_k, num_experts, chunk_rows);
+  if (rc != IQ_OK) return rc;
+  if (!hess || (T != 0 && !x)) return IQ_ERR_NULL;
+  const size_t need = T ? iq::plan_hessian(T, K, ids ? top_k : 0, num_experts, chunk_rows).bytes : 0;
+  if ((rc = check_workspace(need, workspace, workspace_bytes)) != IQ_OK) return rc;
+  return iq::launch_hessian(x, dtype, T, K, ids, ids ? top_k : 0, num_experts, chunk_rows, hess, status, workspace,
+                            stream) == 0
              ? IQ_OK
              : IQ_ERR_HIP;
 }
@@ -105,77 +216,65 @@ int iq_imatrix_merge(const float *src_sums, const int64_t *src_counts, int num_e
                                                                                                  : IQ_ERR_HIP;
 }
 
-static int quantize_common(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
-                           const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
-                           int32_t *status, bool every, hipStream_t stream) {
+int iq_quantize_workspace_size(int fmt, int64_t rows, int64_t cols, int64_t rows_per_expert, int weighted,
+                               size_t *bytes) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;
-  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
-  if (!grid || (rows != 0 && (!w || !out))) return IQ_ERR_NULL;
-  if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
-  if (rows_per_expert < 1 || rows % rows_per_expert != 0) return IQ_ERR_SHAPE;
-  if (cols / 256 > (int64_t(1) << 24) || rows > (int64_t(1) << 40)) return IQ_ERR_SHAPE;
-  iq::EncArgs A{};
-  A.w = w;
-  A.dtype = dtype;
-  A.rows = rows;
-  A.cols = cols;
-  A.rpe = rows_per_expert;
-  A.E = rows / rows_per_expert;
-  A.nb = static_cast<int>(cols / 256);
-  A.grid = grid;
-  A.imp = importance;
-  A.choices = choices;
-  A.out = out;
-  A.copies = every ? kFmt[fmt].num_choices : 1;
-  A.copy_stride = rows * (cols / 256) * kFmt[fmt].block_bytes;
-  A.status = status;
-  // workgroups: experts x 64-row tiles x column sets; must fit one grid dimension
-  const int64_t wgg = (fmt == IQ_FMT_IQ1_M) ? 8 : 4;
-  const int64_t total = A.E * ((rows_per_expert + 63) / 64) * A.nb * (32 / wgg);
-  if (total >= (int64_t(1) << 31)) return IQ_ERR_SHAPE;
-  return iq::launch_quantize(fmt, A, every, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
+  if (!bytes) return IQ_ERR_NULL;
+  const int rc = check_encode_shape(rows, cols, rows_per_expert, fmt, wg_cols(fmt));
+  if (rc != IQ_OK) return rc;
+  *bytes = rows ? iq::plan_quantize(fmt, rows, cols, rows_per_expert, weighted != 0).bytes : 0;
+  return IQ_OK;
 }
 
 int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
-                const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
-                int32_t *status, hipStream_t stream) {
-  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, choices, out, status, false,
-                         stream);
+                const float *grid, const float *importance, const uint8_t *choices, uint8_t *out, void *workspace,
+                size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, choices, out, workspace,
+                         workspace_bytes, status, false, nullptr, nullptr, stream);
+}
+
+int iq_quantize_timed(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                      const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
+                      void *workspace, size_t workspace_bytes, int32_t *status, hipEvent_t search_start,
+                      hipEvent_t search_stop, hipStream_t stream) {
+  if (!search_start || !search_stop) return IQ_ERR_NULL;
+  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, choices, out, workspace,
+                         workspace_bytes, status, false, search_start, search_stop, stream);
 }
 
 int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
-                             const float *grid, const float *importance, uint8_t *out, int32_t *status,
-                             hipStream_t stream) {
-  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, nullptr, out, status, true,
-                         stream);
+                             const float *grid, const float *importance, uint8_t *out, void *workspace,
+                             size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, nullptr, out, workspace,
+                         workspace_bytes, status, true, nullptr, nullptr, stream);
+}
+
+int iq_choice_search_workspace_size(int fmt, int64_t rows, int64_t cols, int64_t rows_per_expert, int weighted,
+                                    size_t *bytes) {
+  if (bad_fmt(fmt)) return IQ_ERR_FMT;
+  if (!bytes) return IQ_ERR_NULL;
+  const int rc = check_encode_shape(rows, cols, rows_per_expert, fmt, wg_cols(fmt));
+  if (rc != IQ_OK) return rc;
+  *bytes = rows ? iq::plan_choice_search(fmt, rows, cols, rows_per_expert, weighted != 0).bytes : 0;
+  return IQ_OK;
 }
 
 int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
                      const float *grid, const float *importance, const float *hess, float perc_damp,
-                     uint8_t *choices, uint8_t *out, int32_t *status, hipStream_t stream) {
+                     uint8_t *choices, uint8_t *out, void *workspace, size_t workspace_bytes, int32_t *status,
+                     hipStream_t stream) {
   if (bad_fmt(fmt)) return IQ_ERR_FMT;
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
   if (!grid || (rows != 0 && (!w || !hess || !choices))) return IQ_ERR_NULL;
-  if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
-  if (rows_per_expert < 1 || rows % rows_per_expert != 0) return IQ_ERR_SHAPE;
-  if (cols / 256 > (int64_t(1) << 24) || rows > (int64_t(1) << 40)) return IQ_ERR_SHAPE;
+  int rc = check_encode_shape(rows, cols, rows_per_expert, fmt, wg_cols(fmt));
+  if (rc != IQ_OK) return rc;
   if (!(perc_damp >= 0.0f) || perc_damp > 3.0e38f) return IQ_ERR_ARG;
-  iq::EncArgs A{};
-  A.w = w;
-  A.dtype = dtype;
-  A.rows = rows;
-  A.cols = cols;
-  A.rpe = rows_per_expert;
-  A.E = rows / rows_per_expert;
-  A.nb = static_cast<int>(cols / 256);
-  A.grid = grid;
-  A.imp = importance;
+  const size_t need =
+      rows ? iq::plan_choice_search(fmt, rows, cols, rows_per_expert, importance != nullptr).bytes : 0;
+  if ((rc = check_workspace(need, workspace, workspace_bytes)) != IQ_OK) return rc;
+  iq::EncArgs A = enc_args(w, dtype, rows, cols, rows_per_expert, grid, importance, status);
   A.out = out;
-  A.status = status;
-  const int64_t wgg = (fmt == IQ_FMT_IQ1_M) ? 8 : 4;
-  const int64_t total = A.E * ((rows_per_expert + 63) / 64) * A.nb * (32 / wgg);
-  if (total >= (int64_t(1) << 31)) return IQ_ERR_SHAPE;
-  return iq::launch_choice_search(fmt, A, hess, perc_damp, choices, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
+  return iq::launch_choice_search(fmt, A, hess, perc_damp, choices, workspace, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
 }
 
 int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
@@ -184,15 +283,9 @@ int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, co
   if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
   if (!grid || (rows != 0 && (!packed || !out))) return IQ_ERR_NULL;
   if (rows < 0 || cols <= 0 || cols % 256 != 0) return IQ_ERR_SHAPE;
-  if (rows * (cols / 256) * 32 / 256 >= (int64_t(1) << 31)) return IQ_ERR_SHAPE;
+  if (rows > (int64_t(1) << 40) / (cols / 256) || rows * (cols / 256) * 32 / 256 >= (int64_t(1) << 31))
+    return IQ_ERR_SHAPE;
   return iq::launch_decode(fmt, packed, rows, cols, grid, out, dtype, stream) == 0 ? IQ_OK : IQ_ERR_HIP;
-}
-
-int iq_time_next_search(hipEvent_t start, hipEvent_t stop) {
-  if ((start == nullptr) != (stop == nullptr)) return IQ_ERR_NULL;
-  t_search_start = start;
-  t_search_stop = stop;
-  return IQ_OK;
 }
 
 const char *iq_error_string(int code) {
@@ -203,7 +296,8 @@ const char *iq_error_string(int code) {
     case IQ_ERR_NULL: return "required pointer is NULL";
     case IQ_ERR_SHAPE: return "invalid shape";
     case IQ_ERR_ARG: return "invalid argument";
-    case IQ_ERR_HIP: return "HIP allocation or launch failure";
+    case IQ_ERR_HIP: return "HIP launch failure";
+    case IQ_ERR_WORKSPACE: return "workspace smaller than the size query returns";
   }
   return "unknown error code";
 }

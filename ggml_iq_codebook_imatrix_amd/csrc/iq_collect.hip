@@ -29,18 +29,20 @@
 
 namespace iq {
 
-// Pass 1 (routed): membership bitmaps bm[chunk][e][words] and a per-token flag
-// for tokens that name one expert twice.  One workgroup per 256 positions of a
-// chunk: it clears its own 8 words of every expert's row (the chunk's last
-// workgroup also the row's tail), then marks.
+// Pass 1 (routed): membership bitmaps bm[chunk - chunk0][e][words] and a
+// per-token flag dup[t - chunk0 * chunk_rows] for tokens that name one expert
+// twice, for the chunks of one window starting at chunk0.  One workgroup per
+// 256 positions of a chunk: it clears its own 8 words of every expert's row
+// (the chunk's last workgroup also the row's tail), then marks.
 __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__restrict__ ids, int64_t T,
                                                              int top_k, int E, int chunk_rows, int W,
-                                                             uint32_t *__restrict__ bm,
+                                                             int64_t chunk0, uint32_t *__restrict__ bm,
                                                              uint8_t *__restrict__ dup, int32_t *status) {
   const int nsub = (chunk_rows + 255) / 256;
-  const int64_t chunk = blockIdx.x / nsub;
+  const int64_t lchunk = blockIdx.x / nsub;
+  const int64_t chunk = chunk0 + lchunk;
   const int sub = static_cast<int>(blockIdx.x % nsub);
-  uint32_t *reg = bm + chunk * static_cast<int64_t>(E) * W;
+  uint32_t *reg = bm + lchunk * static_cast<int64_t>(E) * W;
   const int w0 = sub * 8;
   const int w1 = sub == nsub - 1 ? W : w0 + 8;
   for (int64_t i = threadIdx.x; i < static_cast<int64_t>(E) * (w1 - w0); i += blockDim.x)
@@ -58,13 +60,14 @@ __global__ void __launch_bounds__(256) collect_route_kernel(const int32_t *__res
       for (int s2 = 0; s2 < s; ++s2) rep = rep || ids[(t0 + p) * top_k + s2] == e;
       atomicOr(&reg[static_cast<int64_t>(e) * W + (p >> 5)], 1u << (p & 31));
     }
-    if (dup) dup[t0 + p] = rep ? 1 : 0;
+    if (dup) dup[lchunk * chunk_rows + p] = rep ? 1 : 0;
   }
   raise_status(status, st);
 }
 
 // Pass 2: partial[slice][e][K] = sum over the slice's member tokens (routed to
-// e; dense: all) of x^2.  Workgroup = NW waves over a 512-column tile, 8
+// e; dense: all) of x^2, for the slices of one window (chunks chunk0 on; the
+// bitmaps and repeat flags are the window's).  Workgroup = NW waves over a 512-column tile, 8
 // columns per lane; member m of the slice (ascending tokens, a token routed
 // twice to e counted twice) goes to wave m mod NW, which adds its members in
 // token order, 8 rows per batch of 16-byte loads.  Routed slices (at most 1,024
@@ -77,8 +80,8 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
                                                                  const int32_t *__restrict__ ids, int top_k, int E,
                                                                  int chunk_rows, int W,
                                                                  const uint32_t *__restrict__ bm,
-                                                                 const uint8_t *__restrict__ dup, int nsub,
-                                                                 int slice_len, float *__restrict__ partial,
+                                                                 const uint8_t *__restrict__ dup, int64_t chunk0,
+                                                                 int nsub, int slice_len, float *__restrict__ partial,
                                                                  int64_t *__restrict__ counts, int32_t *status) {
   __shared__ float s_acc[NW][kCTile];
   __shared__ int s_cnt[NW];
@@ -89,7 +92,8 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
   const int64_t rest = blockIdx.x / ntile;  // slice * E + e
   const int e = static_cast<int>(rest % E);
   const int64_t slice = rest / E;
-  const int64_t chunk = slice / nsub;
+  const int64_t lchunk = slice / nsub;
+  const int64_t chunk = chunk0 + lchunk;
   const int sub = static_cast<int>(slice % nsub);
   const int64_t cbase = chunk * chunk_rows;
   const int64_t n = (T - cbase < chunk_rows) ? (T - cbase) : chunk_rows;
@@ -108,7 +112,7 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
       const int64_t nw = (nmem + 31) / 32;
       uint32_t word = 0u;
       if (lane < nw) {
-        word = bm[(chunk * E + e) * W + (p_lo >> 5) + lane];
+        word = bm[(lchunk * E + e) * W + (p_lo >> 5) + lane];
         const int64_t lim = nmem - 32 * static_cast<int64_t>(lane);
         if (lim < 32) word &= (1u << lim) - 1u;
       }
@@ -149,7 +153,7 @@ __global__ void __launch_bounds__(64 * NW) collect_slice_kernel(const void *__re
     if (ROUTED) {
 #pragma unroll
       for (int u = 0; u < kCBatch; ++u) {
-        if (mult[u] && dup[tok[u]]) {  // rare: count the repeats of e in this token's ids
+        if (mult[u] && dup[tok[u] - chunk0 * chunk_rows]) {  // rare: count the repeats of e in this token's ids
           int c = 0;
           for (int s2 = 0; s2 < top_k; ++s2) c += ids[tok[u] * top_k + s2] == e;
           mult[u] = c;
@@ -236,159 +240,166 @@ __global__ void __launch_bounds__(256) collect_combine_kernel(const float *__res
 
 template <int DT, bool VEC, int NW, bool ROUTED>
 static void launch_slices(dim3 g, hipStream_t stream, const void *x, int64_t T, int64_t K, const int32_t *ids,
-                          int top_k, int E, int chunk_rows, int W, const uint32_t *bm, const uint8_t *dup, int nsub,
-                          int slice_len, float *partial, int64_t *counts, int32_t *status) {
+                          int top_k, int E, int chunk_rows, int W, const uint32_t *bm, const uint8_t *dup,
+                          int64_t chunk0, int nsub, int slice_len, float *partial, int64_t *counts,
+                          int32_t *status) {
   hipLaunchKernelGGL((collect_slice_kernel<DT, VEC, NW, ROUTED>), g, dim3(64 * NW), 0, stream, x, T, K, ids, top_k, E,
-                     chunk_rows, W, bm, dup, nsub, slice_len, partial, counts, status);
+                     chunk_rows, W, bm, dup, chunk0, nsub, slice_len, partial, counts, status);
 }
 
-int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
-                   int chunk_rows, float *sums, int64_t *counts, int32_t *status, hipStream_t stream) {
-  if (T == 0) return 0;
-  const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
-  const int W = (chunk_rows + 31) / 32 + 1;
-  const int64_t ntile = (K + kCTile - 1) / kCTile;
-  // dense: 16-wave workgroups, slices sized for >= 128 workgroups; routed:
-  // 4-wave workgroups, slices of at most 1,024 positions and >= 512 workgroups
-#ifndef IQ_COLLECT_DENSE_WGS
-#define IQ_COLLECT_DENSE_WGS 128
-#endif
-  const int64_t want = ids ? 512 : IQ_COLLECT_DENSE_WGS;
-  int64_t nsub = (want + nchunks * E * ntile - 1) / (nchunks * E * ntile);
-  if (ids && nsub < (chunk_rows + kMaxRoutedSlice - 1) / kMaxRoutedSlice)
+// Slices: dense workgroups of 16 waves, routed ones of 4; a window holds
+// enough chunks for ~4,096 (chunk, expert, column tile) units (at least one
+// chunk), and each of its chunks is cut into nsub slices so the window's
+// launch has >= 128 (dense) / 512 (routed) workgroups; routed slices hold at
+// most 1,024 positions.  The partials of a window are added to the sums in
+// slice order before the next window reuses them, which is the same sequence
+// of fp32 additions as one pass over all slices.
+constexpr int64_t kWindowUnits = 4096;
+
+CollectPlan plan_collect(int64_t T, int64_t K, bool routed, int E, int chunk_rows) {
+  CollectPlan p{};
+  p.nchunks = (T + chunk_rows - 1) / chunk_rows;
+  p.W = (chunk_rows + 31) / 32 + 1;
+  p.ntile = (K + kCTile - 1) / kCTile;
+  const int64_t units = static_cast<int64_t>(E) * p.ntile;  // per chunk
+  int64_t wc = (kWindowUnits + units - 1) / units;
+  p.wchunks = p.nchunks < wc ? p.nchunks : wc;
+  if (p.wchunks < 1) p.wchunks = 1;
+  const int64_t want = routed ? 512 : 128;
+  int64_t nsub = (want + p.wchunks * units - 1) / (p.wchunks * units);
+  if (routed && nsub < (chunk_rows + kMaxRoutedSlice - 1) / kMaxRoutedSlice)
     nsub = (chunk_rows + kMaxRoutedSlice - 1) / kMaxRoutedSlice;
   const int64_t max_sub = (chunk_rows + 31) / 32;
   if (nsub > max_sub) nsub = max_sub;
   if (nsub < 1) nsub = 1;
-  const int64_t slice_len = ((chunk_rows + nsub - 1) / nsub + 31) / 32 * 32;
-  nsub = (chunk_rows + slice_len - 1) / slice_len;
-  const int64_t nslices = nchunks * nsub;
+  p.slice_len = ((chunk_rows + nsub - 1) / nsub + 31) / 32 * 32;
+  p.nsub = (chunk_rows + p.slice_len - 1) / p.slice_len;
+  const size_t pbytes = static_cast<size_t>(p.wchunks) * p.nsub * E * K * sizeof(float);
+  const size_t bbytes = routed ? static_cast<size_t>(p.wchunks) * E * p.W * sizeof(uint32_t) : 0;
+  const size_t dbytes = routed ? static_cast<size_t>(p.wchunks) * chunk_rows : 0;
+  p.boff = ws_up(pbytes);
+  p.doff = p.boff + ws_up(bbytes);
+  p.bytes = p.doff + ws_up(dbytes) + kWsAlign;
+  return p;
+}
+
+int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
+                   int chunk_rows, float *sums, int64_t *counts, int32_t *status, void *ws, hipStream_t stream) {
+  if (T == 0) return 0;
+  const CollectPlan P = plan_collect(T, K, ids != nullptr, E, chunk_rows);
+  char *base = ws_base(ws);
+  float *partial = reinterpret_cast<float *>(base);
+  uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(base + P.boff) : nullptr;
+  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(base + P.doff) : nullptr;
   const int64_t EK = static_cast<int64_t>(E) * K;
-  const size_t pbytes = static_cast<size_t>(nslices) * EK * sizeof(float);
-  const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
-  const size_t dbytes = ids ? static_cast<size_t>(T) : 0;
-  const size_t boff = (pbytes + 255) & ~size_t(255), doff = boff + ((bbytes + 255) & ~size_t(255));
-  void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, doff + dbytes + 256, stream) != hipSuccess) return -1;
-  float *partial = static_cast<float *>(scratch);
-  uint32_t *bm = reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + boff);
-  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(static_cast<char *>(scratch) + doff) : nullptr;
-  if (ids)
-    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
-                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, dup, status);
-  const dim3 g2(static_cast<unsigned>(nslices * E * ntile));
   const bool vec = K % kCPL == 0;  // 16-byte (bf16) / 32-byte (f32) aligned rows, whole 8-column lanes
-  const int ns = static_cast<int>(nsub), sl = static_cast<int>(slice_len);
-  const uint32_t *bmc = bm;
-  auto go = [&](auto dt, auto v, auto nw, auto r) {
-    launch_slices<decltype(dt)::value, decltype(v)::value, decltype(nw)::value, decltype(r)::value>(
-        g2, stream, x, T, K, ids, top_k, E, chunk_rows, W, bmc, dup, ns, sl, partial, counts, status);
-  };
+  const int ns = static_cast<int>(P.nsub), sl = static_cast<int>(P.slice_len);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using BT = std::true_type;
   using BF = std::false_type;
   using WR = std::integral_constant<int, 4>;
   using WD = std::integral_constant<int, 16>;
-  if (ids) {
-    if (dtype == 1) { if (vec) go(I1{}, BT{}, WR{}, BT{}); else go(I1{}, BF{}, WR{}, BT{}); }
-    else { if (vec) go(I0{}, BT{}, WR{}, BT{}); else go(I0{}, BF{}, WR{}, BT{}); }
-  } else {
-    if (dtype == 1) { if (vec) go(I1{}, BT{}, WD{}, BF{}); else go(I1{}, BF{}, WD{}, BF{}); }
-    else { if (vec) go(I0{}, BT{}, WD{}, BF{}); else go(I0{}, BF{}, WD{}, BF{}); }
+  for (int64_t c0 = 0; c0 < P.nchunks; c0 += P.wchunks) {
+    const int64_t nc = P.nchunks - c0 < P.wchunks ? P.nchunks - c0 : P.wchunks;
+    const int64_t nslices = nc * P.nsub;
+    if (ids) {
+      hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nc * ((chunk_rows + 255) / 256))),
+                         dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, P.W, c0, bm, dup, status);
+      if (hipGetLastError() != hipSuccess) return -1;
+    }
+    const dim3 g2(static_cast<unsigned>(nslices * E * P.ntile));
+    const uint32_t *bmc = bm;
+    auto go = [&](auto dt, auto v, auto nw, auto r) {
+      launch_slices<decltype(dt)::value, decltype(v)::value, decltype(nw)::value, decltype(r)::value>(
+          g2, stream, x, T, K, ids, top_k, E, chunk_rows, P.W, bmc, dup, c0, ns, sl, partial, counts, status);
+    };
+    if (ids) {
+      if (dtype == 1) { if (vec) go(I1{}, BT{}, WR{}, BT{}); else go(I1{}, BF{}, WR{}, BT{}); }
+      else { if (vec) go(I0{}, BT{}, WR{}, BT{}); else go(I0{}, BF{}, WR{}, BT{}); }
+    } else {
+      if (dtype == 1) { if (vec) go(I1{}, BT{}, WD{}, BF{}); else go(I1{}, BF{}, WD{}, BF{}); }
+      else { if (vec) go(I0{}, BT{}, WD{}, BF{}); else go(I0{}, BF{}, WD{}, BF{}); }
+    }
+    if (hipGetLastError() != hipSuccess) return -1;
+    hipLaunchKernelGGL(collect_combine_kernel, dim3(static_cast<unsigned>((EK + 255) / 256)), dim3(256), 0, stream,
+                       partial, nslices, EK, sums, counts, (ids || c0 > 0) ? int64_t(0) : T);
+    if (hipGetLastError() != hipSuccess) return -1;
   }
-  hipLaunchKernelGGL(collect_combine_kernel, dim3(static_cast<unsigned>((EK + 255) / 256)), dim3(256), 0, stream,
-                     partial, nslices, EK, sums, counts, ids ? int64_t(0) : T);
-  const hipError_t le = hipGetLastError();
-  hipFreeAsync(scratch, stream);
-  return le == hipSuccess ? 0 : -1;
+  return 0;
 }
 
 // ---------------------------------------------------------------------------
-// Importance.  a_j = sqrt(max(m_j, floor_rel * mean)), m_j = sums_j / count.
-// The mean is defined through an exact fixed-point sum so that any reduction
-// order gives the same bits: with M = max_j m_j = f 2^eM (f in [0.5, 1)),
-// L = ceil(log2 K) and s = 62 - eM - L, total = sum_j floor(m_j 2^s) is an
-// integer below 2^62 and mean = fp32(fp64(total) 2^-s / K).
+// Importance.  a_j = sqrt(max(m_j, floor_rel * mean)), m_j = sums_j / count
+// (IEEE fp32 division and square root).  The mean is the plain one: the m_j
+// added one after another in fp64, j ascending from 0, the total divided by K
+// in fp64 and rounded to fp32.  That running sum is one dependent chain: wave 0
+// walks it 64 values at a time (each lane converts one m_j, a lane read hands
+// it to the chain), prefetching the next 64 while it adds; the other waves
+// meanwhile form the m_j and check them.  Lanes past K add +0.0, which leaves
+// the sum unchanged (it starts at +0 and only meets non-negative values unless
+// the expert is flagged, and then its weights are flat anyway).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t fixed_term(float m, int s) {
-  const uint32_t bits = __float_as_uint(m);
-  const uint32_t eb = (bits >> 23) & 0xffu;
-  const uint64_t mant = eb ? ((bits & 0x7fffffu) | 0x800000u) : (bits & 0x7fffffu);
-  const int ex = eb ? static_cast<int>(eb) - 150 : -149;
-  const int sh = ex + s;
-  if (sh >= 0) return mant << sh;
-  if (-sh >= 64) return 0;
-  return mant >> (-sh);
-}
-
-__device__ __forceinline__ int frexp_exponent(float m) {  // m > 0: m = f 2^e, f in [0.5, 1)
-  const uint32_t bits = __float_as_uint(m);
-  const uint32_t eb = (bits >> 23) & 0xffu;
-  if (eb) return static_cast<int>(eb) - 126;
-  return (32 - __builtin_clz(bits & 0x7fffffu)) - 149;
+__device__ __forceinline__ double lane_value(double v, int l) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
 __global__ void __launch_bounds__(1024) importance_kernel(const float *__restrict__ sums,
                                                           const int64_t *__restrict__ counts, int64_t K,
-                                                          float floor_rel, int L, float *__restrict__ imp,
+                                                          float floor_rel, float *__restrict__ imp,
                                                           int32_t *status) {
   constexpr int NT = 1024, NW = NT / 64;
-  __shared__ float s_f[NW];
   __shared__ int s_i[NW];
-  __shared__ unsigned long long s_u[NW];
+  __shared__ float s_mean;
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *se = sums + static_cast<int64_t>(e) * K;
   float *ie = imp + static_cast<int64_t>(e) * K;
   const int64_t c = counts[e];
-  bool flat = c <= 0;
-  float mx = 0.0f;
-  int bad = 0;
-  if (!flat) {
-    const float fc = static_cast<float>(c);
-    for (int64_t j = tid; j < K; j += NT) {
-      const float m = se[j] / fc;
-      bad |= !(finite_f(m) && m >= 0.0f);
-      mx = fmaxf(mx, m);
-      ie[j] = m;  // m_j kept in the output until the floor is known
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, o));
-      bad |= __shfl_xor(bad, o);
-    }
-    if (lane == 0) { s_f[wave] = mx; s_i[wave] = bad; }
-    __syncthreads();
-    mx = s_f[0];
-    bad = s_i[0];
-    for (int w = 1; w < NW; ++w) { mx = fmaxf(mx, s_f[w]); bad |= s_i[w]; }
-    if (bad && tid == 0) raise_status(status, ST_BADIMP);
-    flat = bad || mx == 0.0f;
-  }
-  if (flat) {
-    __syncthreads();
+  if (c <= 0) {  // idle expert: flat weights
     for (int64_t j = tid; j < K; j += NT) ie[j] = 1.0f;
     return;
   }
-  const int s = 62 - frexp_exponent(mx) - L;
-  unsigned long long tot = 0;
-  for (int64_t j = tid; j < K; j += NT) tot += fixed_term(ie[j], s);
-  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-  if (lane == 0) s_u[wave] = tot;
+  const float fc = static_cast<float>(c);
+  int bad = 0;
+  for (int64_t j = tid; j < K; j += NT) {
+    const float m = se[j] / fc;
+    bad |= !(finite_f(m) && m >= 0.0f);
+    ie[j] = m;  // m_j kept in the output until the floor is known
+  }
+  for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
+  if (lane == 0) s_i[wave] = bad;
+  if (wave == 0) {
+    double acc = 0.0;
+    float nxt = lane < K ? se[lane] : 0.0f;
+    for (int64_t j0 = 0; j0 < K; j0 += 64) {
+      const double v = j0 + lane < K ? static_cast<double>(nxt / fc) : 0.0;
+      nxt = j0 + 64 + lane < K ? se[j0 + 64 + lane] : 0.0f;
+#pragma unroll
+      for (int l = 0; l < 64; ++l) acc = acc + lane_value(v, l);
+    }
+    if (lane == 0) s_mean = static_cast<float>(acc / static_cast<double>(K));
+  }
   __syncthreads();
-  tot = 0;
-  for (int w = 0; w < NW; ++w) tot += s_u[w];
-  const float mean = static_cast<float>(ldexp(static_cast<double>(tot), -s) / static_cast<double>(K));
+  bad = 0;
+  for (int w = 0; w < NW; ++w) bad |= s_i[w];
+  const float mean = s_mean;
+  if (bad && tid == 0) raise_status(status, ST_BADIMP);
+  if (bad || mean == 0.0f) {  // nothing usable: flat weights
+    for (int64_t j = tid; j < K; j += NT) ie[j] = 1.0f;
+    return;
+  }
   const float fl = floor_rel * mean;
   for (int64_t j = tid; j < K; j += NT) ie[j] = sqrtf(fmaxf(ie[j], fl));
 }
 
 int launch_importance(const float *sums, const int64_t *counts, int E, int64_t K, float floor_rel, float *imp,
                       int32_t *status, hipStream_t stream) {
-  int L = 0;
-  while ((int64_t(1) << L) < K) ++L;
   hipLaunchKernelGGL(importance_kernel, dim3(static_cast<unsigned>(E)), dim3(1024), 0, stream, sums, counts, K,
-                     floor_rel, L, imp, status);
+                     floor_rel, imp, status);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -899,101 +910,116 @@ __global__ void __launch_bounds__(256) hessian_combine_routed_kernel(const float
   *d = *d + s;
 }
 
-int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
-                   int chunk_rows, float *hess, int32_t *status, hipStream_t stream) {
-  if (T == 0) return 0;
-  const int64_t nchunks = (T + chunk_rows - 1) / chunk_rows;
-  const int W = (chunk_rows + 31) / 32 + 1;
+// Dense: uniform token splits, enough waves for 256 CUs with at least 256
+// tokens each.  Routed: an expert whose list holds more than `target` entries
+// is cut into ceil(len / target) splits, target sized for ~2,048 workgroups
+// over the launch (256 .. 1,024 entries), so the busiest expert's lists do not
+// run as one serial chain; the cut experts' partials stay within 512 MiB.
+HessPlan plan_hessian(int64_t T, int64_t K, int top_k, int E, int chunk_rows) {
+  HessPlan p{};
+  const bool routed = top_k > 0;
+  p.nchunks = (T + chunk_rows - 1) / chunk_rows;
+  p.W = (chunk_rows + 31) / 32 + 1;
   const int64_t nb = K / 256;
   const int64_t ntiles = static_cast<int64_t>(E) * nb * 10;
   const int64_t per_e = nb * 65536;  // floats of one expert's blocks
   const int64_t hn = static_cast<int64_t>(E) * per_e;
-  // Dense: uniform token splits, enough waves for 256 CUs with at least 256
-  // tokens each.  Routed: an expert whose list holds more than `target` entries
-  // is cut into ceil(len / target) splits, target sized for ~2,048 workgroups
-  // over the launch (256 .. 1,024 entries), so the busiest expert's lists do not
-  // run as one serial chain; the cut experts' partials stay within 512 MiB.
-  int64_t nsplit = 1, split_len = T, target = 0, smax = 0, pmax = 0, hmax = 0;
-  if (!ids) {
+  p.nsplit = 1;
+  p.split_len = T;
+  if (!routed) {
     if (ntiles < 2048) {
-      nsplit = (2048 + ntiles - 1) / ntiles;
+      p.nsplit = (2048 + ntiles - 1) / ntiles;
       const int64_t by_tokens = (T + 255) / 256;
-      if (nsplit > by_tokens) nsplit = by_tokens;
-      if (nsplit < 1) nsplit = 1;
+      if (p.nsplit > by_tokens) p.nsplit = by_tokens;
+      if (p.nsplit < 1) p.nsplit = 1;
     }
-    split_len = ((T + nsplit - 1) / nsplit + kHTok - 1) / kHTok * kHTok;
-    nsplit = (T + split_len - 1) / split_len;
+    p.split_len = ((T + p.nsplit - 1) / p.nsplit + kHTok - 1) / kHTok * kHTok;
+    if (p.split_len < kHTok) p.split_len = kHTok;
+    p.nsplit = (T + p.split_len - 1) / p.split_len;
   } else {
     const int64_t total = T * top_k;
-    target = (total * nb * 10 + 2047) / 2048;
-    target = target < 256 ? 256 : (target > 1024 ? 1024 : target);
-    target = (target + kHTok - 1) / kHTok * kHTok;
+    p.target = (total * nb * 10 + 2047) / 2048;
+    p.target = p.target < 256 ? 256 : (p.target > 1024 ? 1024 : p.target);
+    p.target = (p.target + kHTok - 1) / kHTok * kHTok;
     auto ceil_div = [](int64_t a, int64_t d) { return (a + d - 1) / d; };
     // partial slots: only cut experts hold them, fewer than 2 total / target
-    pmax = 2 * ceil_div(total, target);
-    while (pmax > 2 && pmax * per_e * static_cast<int64_t>(sizeof(float)) > (int64_t(512) << 20)) {
-      target *= 2;
-      pmax = 2 * ceil_div(total, target);
+    p.pmax = 2 * ceil_div(total, p.target);
+    while (p.pmax > 2 && p.pmax * per_e * static_cast<int64_t>(sizeof(float)) > (int64_t(512) << 20)) {
+      p.target *= 2;
+      p.pmax = 2 * ceil_div(total, p.target);
     }
-    smax = E + ceil_div(total, target);  // sum over experts of max(1, ceil(len / target))
-    hmax = ceil_div(total, target);      // cut experts: each holds more than target entries
-    if (hmax > E) hmax = E;
+    p.smax = E + ceil_div(total, p.target);  // sum over experts of max(1, ceil(len / target))
+    p.hmax = ceil_div(total, p.target);      // cut experts: each holds more than target entries
+    if (p.hmax > E) p.hmax = E;
   }
-  // scratch: split partials; routed: bitmaps, repeat flags, list lengths and
-  // starts (entries, split slots, partial slots), the cut experts, lists
-  const size_t pbytes = ids ? static_cast<size_t>(pmax) * per_e * sizeof(float)
-                            : (nsplit > 1 ? static_cast<size_t>(nsplit) * hn * sizeof(float) : 0);
-  const size_t bbytes = ids ? static_cast<size_t>(nchunks) * E * W * sizeof(uint32_t) : 0;
-  const size_t dbytes = ids ? static_cast<size_t>(T) : 0;
-  const size_t nbytes = ids ? static_cast<size_t>(4 * E + 3) * sizeof(int64_t) + (E + 1) * sizeof(int32_t) : 0;
-  const size_t lbytes = ids ? static_cast<size_t>(T) * top_k * sizeof(uint32_t) : 0;
-  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
-  const size_t off_b = up(pbytes), off_d = off_b + up(bbytes), off_n = off_d + up(dbytes), off_l = off_n + up(nbytes);
-  void *scratch = nullptr;
-  if (off_l + lbytes > 0 && hipMallocAsync(&scratch, off_l + lbytes + 256, stream) != hipSuccess) return -1;
-  char *base = static_cast<char *>(scratch);
+  const size_t pbytes = routed ? static_cast<size_t>(p.pmax) * per_e * sizeof(float)
+                               : (p.nsplit > 1 ? static_cast<size_t>(p.nsplit) * hn * sizeof(float) : 0);
+  const size_t bbytes = routed ? static_cast<size_t>(p.nchunks) * E * p.W * sizeof(uint32_t) : 0;
+  const size_t dbytes = routed ? static_cast<size_t>(T) : 0;
+  const size_t nbytes = routed ? static_cast<size_t>(4 * E + 3) * sizeof(int64_t) + (E + 1) * sizeof(int32_t) : 0;
+  const size_t lbytes = routed ? static_cast<size_t>(T) * top_k * sizeof(uint32_t) : 0;
+  p.off_b = ws_up(pbytes);
+  p.off_d = p.off_b + ws_up(bbytes);
+  p.off_n = p.off_d + ws_up(dbytes);
+  p.off_l = p.off_n + ws_up(nbytes);
+  p.bytes = p.off_l + ws_up(lbytes) + kWsAlign;
+  return p;
+}
+
+int launch_hessian(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k, int E,
+                   int chunk_rows, float *hess, int32_t *status, void *ws, hipStream_t stream) {
+  if (T == 0) return 0;
+  const HessPlan P = plan_hessian(T, K, ids ? top_k : 0, E, chunk_rows);
+  const int64_t nb = K / 256;
+  const int64_t ntiles = static_cast<int64_t>(E) * nb * 10;
+  const int64_t per_e = nb * 65536;
+  const int64_t hn = static_cast<int64_t>(E) * per_e;
+  char *base = ws_base(ws);
   float *partial = reinterpret_cast<float *>(base);
-  uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(base + off_b) : nullptr;
-  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(base + off_d) : nullptr;
-  int64_t *lens = ids ? reinterpret_cast<int64_t *>(base + off_n) : nullptr;
+  uint32_t *bm = ids ? reinterpret_cast<uint32_t *>(base + P.off_b) : nullptr;
+  uint8_t *dup = ids ? reinterpret_cast<uint8_t *>(base + P.off_d) : nullptr;
+  int64_t *lens = ids ? reinterpret_cast<int64_t *>(base + P.off_n) : nullptr;
   int64_t *lstart = ids ? lens + E : nullptr;
   int64_t *sstart = ids ? lstart + (E + 1) : nullptr;
   int64_t *pstart = ids ? sstart + (E + 1) : nullptr;
   int32_t *heavy = ids ? reinterpret_cast<int32_t *>(pstart + (E + 1)) : nullptr;
-  uint32_t *list = ids ? reinterpret_cast<uint32_t *>(base + off_l) : nullptr;
+  uint32_t *list = ids ? reinterpret_cast<uint32_t *>(base + P.off_l) : nullptr;
   if (ids) {
-    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(nchunks * ((chunk_rows + 255) / 256))),
-                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, W, bm, dup, status);
+    hipLaunchKernelGGL(collect_route_kernel, dim3(static_cast<unsigned>(P.nchunks * ((chunk_rows + 255) / 256))),
+                       dim3(256), 0, stream, ids, T, top_k, E, chunk_rows, P.W, int64_t(0), bm, dup, status);
+    if (hipGetLastError() != hipSuccess) return -1;
     hipLaunchKernelGGL(route_count_kernel, dim3(static_cast<unsigned>((E + 3) / 4)), dim3(256), 0, stream,
-                       static_cast<const uint32_t *>(bm), nchunks, E, W, lens);
+                       static_cast<const uint32_t *>(bm), P.nchunks, E, P.W, lens);
+    if (hipGetLastError() != hipSuccess) return -1;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, static_cast<const int64_t *>(lens), E,
-                       target, lstart, sstart, pstart, heavy);
+                       P.target, lstart, sstart, pstart, heavy);
+    if (hipGetLastError() != hipSuccess) return -1;
     hipLaunchKernelGGL(route_list_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream,
-                       static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), nchunks, E, W,
+                       static_cast<const uint32_t *>(bm), static_cast<const uint8_t *>(dup), P.nchunks, E, P.W,
                        chunk_rows, static_cast<const int64_t *>(lstart), list);
+    if (hipGetLastError() != hipSuccess) return -1;
   }
-  const dim3 g(static_cast<unsigned>(ids ? smax * nb * 10 : ntiles * nsplit));
+  const dim3 g(static_cast<unsigned>(ids ? P.smax * nb * 10 : ntiles * P.nsplit));
   if (dtype == 1)
     hipLaunchKernelGGL(hessian_kernel<1>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E,
                        static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart),
-                       static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart), nsplit, split_len,
-                       hess, partial, status);
+                       static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart), P.nsplit,
+                       P.split_len, hess, partial, status);
   else
     hipLaunchKernelGGL(hessian_kernel<0>, g, dim3(64), 0, stream, x, T, K, ids, top_k, E,
                        static_cast<const uint32_t *>(list), static_cast<const int64_t *>(lstart),
-                       static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart), nsplit, split_len,
-                       hess, partial, status);
+                       static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart), P.nsplit,
+                       P.split_len, hess, partial, status);
+  if (hipGetLastError() != hipSuccess) return -1;
   if (ids)
-    hipLaunchKernelGGL(hessian_combine_routed_kernel, dim3(static_cast<unsigned>(hmax * ((per_e + 255) / 256))),
+    hipLaunchKernelGGL(hessian_combine_routed_kernel, dim3(static_cast<unsigned>(P.hmax * ((per_e + 255) / 256))),
                        dim3(256), 0, stream, static_cast<const float *>(partial),
                        static_cast<const int64_t *>(sstart), static_cast<const int64_t *>(pstart),
                        static_cast<const int32_t *>(heavy), E, per_e, hess);
-  else if (nsplit > 1)
+  else if (P.nsplit > 1)
     hipLaunchKernelGGL(hessian_combine_kernel, dim3(static_cast<unsigned>((hn + 255) / 256)), dim3(256), 0, stream,
-                       static_cast<const float *>(partial), nsplit, hn, hess);
-  const hipError_t le = hipGetLastError();
-  if (scratch) hipFreeAsync(scratch, stream);
-  return le == hipSuccess ? 0 : -1;
+                       static_cast<const float *>(partial), P.nsplit, hn, hess);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace iq

@@ -66,17 +66,23 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total) {
 
 // ---------------------------------------------------------------------------
 // Importance check: one wave per (expert, block), 4 values per lane;
-// flags[e * nb + b] = 1 when the block's 256 importance values hold a
-// non-finite or negative value.
+// flags[e * nb + b] = 1 when the block's 256 importance values hold a value
+// outside [0, 2^64]: NaN, negative, or above any floored square root of a
+// finite fp32 second moment (sqrt(FLT_MAX) < 2^64).  Within that range, and
+// with a finite fp16 block scale, every fp32 intermediate of the search stays
+// finite (the largest, a unit score, is below 1e34).
 // ---------------------------------------------------------------------------
+constexpr float kImpMax = 18446744073709551616.0f;  // 2^64
+
+__device__ __forceinline__ bool imp_ok(float a) { return a >= 0.0f && a <= kImpMax; }
+
 __device__ __forceinline__ void impcheck_block(int64_t blk, const float *__restrict__ imp, int64_t n,
                                                uint8_t *__restrict__ flags) {
   const int64_t i = blk * 4 + (threadIdx.x >> 6);  // (e * nb + b)
   const int lane = threadIdx.x & 63;
   if (i >= n) return;
   const float4 q = reinterpret_cast<const float4 *>(imp + i * 256)[lane];  // cols = nb * 256
-  const bool ok = finite_f(q.x) && finite_f(q.y) && finite_f(q.z) && finite_f(q.w) && q.x >= 0.0f &&
-                  q.y >= 0.0f && q.z >= 0.0f && q.w >= 0.0f;
+  const bool ok = imp_ok(q.x) && imp_ok(q.y) && imp_ok(q.z) && imp_ok(q.w);
   const uint64_t bad = __ballot(!ok);
   if (lane == 0) flags[i] = bad ? 1 : 0;
 }
@@ -1376,40 +1382,67 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
 }
 
 // ---------------------------------------------------------------------------
-// Host launchers
+// Host launchers.  Workspace plans first (pure functions of the sizes), then
+// the launches: each is checked, and a failed launch returns at once.
 // ---------------------------------------------------------------------------
+namespace {
+constexpr int kGridN[5] = {256, 512, 1024, 2048, 2048};
+constexpr int kNC[5] = {16, 16, 16, 16, 8};
+bool launched_ok() { return hipGetLastError() == hipSuccess; }
+}  // namespace
+
+QuantPlan plan_quantize(int fmt, int64_t rows, int64_t cols, int64_t rpe, bool weighted) {
+  QuantPlan p{};
+  const int64_t nb = cols / 256, E = rows / rpe;
+  const int NG = fmt >= IQ1_S ? 2 : 1;
+  p.ntab = weighted ? E * (cols / 8) : 1;
+  const size_t gbytes = static_cast<size_t>(p.ntab) * NG * kGridN[fmt] * sizeof(float);
+  const size_t dbytes = static_cast<size_t>(rows) * nb * sizeof(uint16_t);
+  const size_t fbytes = weighted ? static_cast<size_t>(E) * nb : 0;
+  p.goff = 0;
+  p.doff = ws_up(gbytes);
+  p.foff = p.doff + ws_up(dbytes);
+  p.bytes = p.foff + ws_up(fbytes) + kWsAlign;
+  return p;
+}
+
+ChoicePlan plan_choice_search(int fmt, int64_t rows, int64_t cols, int64_t rpe, bool weighted) {
+  ChoicePlan p{};
+  const int64_t nblocks = rows * (cols / 256), nl = (rows / rpe) * (cols / 256);
+  p.q = plan_quantize(fmt, rows, cols, rpe, weighted);
+  p.roff = 0;
+  p.loff = ws_up(static_cast<size_t>(kNC[fmt]) * nblocks * 32 * sizeof(uint32_t));
+  p.qoff = p.loff + ws_up(static_cast<size_t>(nl) * sizeof(float));
+  p.bytes = p.qoff + p.q.bytes;  // the encoder part keeps its own slack
+  return p;
+}
+
 template <int F>
-static int launch_quantize_t(EncArgs A, int mode, hipStream_t stream) {
+static int launch_quantize_t(EncArgs A, int mode, void *ws, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
   using G = Geo<F>;
   const int64_t nblocks = A.rows * A.nb;
   if (nblocks == 0) return 0;
-  const int64_t cgs = A.cols / 8;
-  const int64_t ntab = A.imp ? A.E * cgs : 1;
+  const QuantPlan P = plan_quantize(F, A.rows, A.cols, A.rpe, A.imp != nullptr);
   const int NG = G::IQ1 ? 2 : 1;
-  const size_t gbytes = static_cast<size_t>(ntab) * NG * G::N * sizeof(float);
-  const size_t dbytes = static_cast<size_t>(nblocks) * sizeof(uint16_t);
-  const size_t fbytes = A.imp ? static_cast<size_t>(A.E) * A.nb : 0;
-  const size_t goff = 0, doff = (gbytes + 255) & ~size_t(255), foff = doff + ((dbytes + 255) & ~size_t(255));
-  void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, foff + fbytes + 256, stream) != hipSuccess) return -1;
-  char *base = static_cast<char *>(scratch);
-  A.gtab = reinterpret_cast<float *>(base + goff);
-  A.dscr = reinterpret_cast<uint16_t *>(base + doff);
-  uint8_t *impflags = A.imp ? reinterpret_cast<uint8_t *>(base + foff) : nullptr;
+  const int64_t cgs = A.cols / 8;
+  char *base = ws_base(ws);
+  A.gtab = reinterpret_cast<float *>(base + P.goff);
+  A.dscr = reinterpret_cast<uint16_t *>(base + P.doff);
+  uint8_t *impflags = A.imp ? reinterpret_cast<uint8_t *>(base + P.foff) : nullptr;
   A.gtab_e_stride = A.imp ? cgs * NG * G::N : 0;
   A.gtab_cg_stride = A.imp ? NG * G::N : 0;
-
-  const int64_t gblocks = (ntab * G::N + 255) / 256;
-  const int64_t nf = impflags ? A.E * A.nb : 0;
-  hipLaunchKernelGGL(prep_kernel<F>, dim3(static_cast<unsigned>(gblocks + (nf + 3) / 4)), dim3(256), 0, stream,
-                     A.grid, A.imp, ntab, A.gtab, gblocks, nf, impflags);
-  hipLaunchKernelGGL(anchor_kernel<F>, dim3(static_cast<unsigned>((nblocks + 7) / 8)), dim3(256), 0, stream, A,
-                     static_cast<const uint8_t *>(impflags));
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb * (32 / G::WGG);
-  hipEvent_t ev0, ev1;
-  take_search_events(&ev0, &ev1);
-  if (ev0) hipEventRecord(ev0, stream);
+
+  const int64_t gblocks = (P.ntab * G::N + 255) / 256;
+  const int64_t nf = impflags ? A.E * A.nb : 0;
+  hipLaunchKernelGGL(prep_kernel<F>, dim3(static_cast<unsigned>(gblocks + (nf + 3) / 4)), dim3(256), 0, stream,
+                     A.grid, A.imp, P.ntab, A.gtab, gblocks, nf, impflags);
+  if (!launched_ok()) return -1;
+  hipLaunchKernelGGL(anchor_kernel<F>, dim3(static_cast<unsigned>((nblocks + 7) / 8)), dim3(256), 0, stream, A,
+                     static_cast<const uint8_t *>(impflags));
+  if (!launched_ok()) return -1;
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return -1;
   const dim3 grid_dim(static_cast<unsigned>(A.total_wg)), block_dim(64 * G::WGG);
   if (mode == RECORDS)
     hipLaunchKernelGGL((search_kernel<F, RECORDS>), grid_dim, block_dim, 0, stream, A);
@@ -1419,21 +1452,19 @@ static int launch_quantize_t(EncArgs A, int mode, hipStream_t stream) {
     hipLaunchKernelGGL((search_kernel<F, FIXED_CHOICES>), grid_dim, block_dim, 0, stream, A);
   else
     hipLaunchKernelGGL((search_kernel<F, SEARCH>), grid_dim, block_dim, 0, stream, A);
-  hipError_t le = hipGetLastError();
-  if (ev1) hipEventRecord(ev1, stream);
-  if (le == hipSuccess && A.d_out)
-    le = hipMemcpyAsync(A.d_out, A.dscr, dbytes, hipMemcpyDeviceToDevice, stream);
-  hipFreeAsync(scratch, stream);
-  return le == hipSuccess ? 0 : -1;
+  if (!launched_ok()) return -1;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return -1;
+  return 0;
 }
 
-int launch_quantize(int fmt, EncArgs A, bool every, hipStream_t stream) {
+int launch_quantize(int fmt, EncArgs A, bool every, void *ws, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+  const int mode = every ? EVERY : SEARCH;
   switch (fmt) {
-    case IQ2_XXS: return launch_quantize_t<IQ2_XXS>(A, every ? EVERY : SEARCH, stream);
-    case IQ2_XS: return launch_quantize_t<IQ2_XS>(A, every ? EVERY : SEARCH, stream);
-    case IQ2_S: return launch_quantize_t<IQ2_S>(A, every ? EVERY : SEARCH, stream);
-    case IQ1_S: return launch_quantize_t<IQ1_S>(A, every ? EVERY : SEARCH, stream);
-    case IQ1_M: return launch_quantize_t<IQ1_M>(A, every ? EVERY : SEARCH, stream);
+    case IQ2_XXS: return launch_quantize_t<IQ2_XXS>(A, mode, ws, ev0, ev1, stream);
+    case IQ2_XS: return launch_quantize_t<IQ2_XS>(A, mode, ws, ev0, ev1, stream);
+    case IQ2_S: return launch_quantize_t<IQ2_S>(A, mode, ws, ev0, ev1, stream);
+    case IQ1_S: return launch_quantize_t<IQ1_S>(A, mode, ws, ev0, ev1, stream);
+    case IQ1_M: return launch_quantize_t<IQ1_M>(A, mode, ws, ev0, ev1, stream);
   }
   return -1;
 }
@@ -1445,7 +1476,7 @@ static int launch_decode_t(const uint8_t *packed, int64_t rows, int64_t cols, co
   if (ng == 0) return 0;
   hipLaunchKernelGGL(decode_kernel<F>, dim3(static_cast<unsigned>((ng + 255) / 256)), dim3(256), 0, stream,
                      packed, ng, grid, out, dtype);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return launched_ok() ? 0 : -1;
 }
 
 int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid, void *out,
@@ -1461,47 +1492,44 @@ int launch_decode(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, co
 }
 
 template <int F>
-static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp, uint8_t *choices,
+static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp, uint8_t *choices, void *ws,
                                   hipStream_t stream) {
   using G = Geo<F>;
   const int64_t nblocks = A.rows * A.nb;
   if (nblocks == 0) return 0;
   const int64_t nl = A.E * A.nb;
-  const size_t rbytes = static_cast<size_t>(G::NC) * nblocks * 32 * sizeof(uint32_t);
-  const size_t doff = (rbytes + 255) & ~size_t(255);
-  const size_t loff = doff + ((nblocks * sizeof(uint16_t) + 255) & ~size_t(255));
-  void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, loff + nl * sizeof(float), stream) != hipSuccess) return -1;
-  uint32_t *rec = static_cast<uint32_t *>(scratch);
-  uint16_t *dblk = reinterpret_cast<uint16_t *>(static_cast<char *>(scratch) + doff);
-  float *lam = reinterpret_cast<float *>(static_cast<char *>(scratch) + loff);
+  const ChoicePlan P = plan_choice_search(F, A.rows, A.cols, A.rpe, A.imp != nullptr);
+  char *base = ws_base(ws);
+  uint32_t *rec = reinterpret_cast<uint32_t *>(base + P.roff);
+  float *lam = reinterpret_cast<float *>(base + P.loff);
+  void *qws = base + P.qoff;
+  // the record sweep's fp16 block scales, read by the choice search
+  const uint16_t *dblk = reinterpret_cast<const uint16_t *>(ws_base(qws) + P.q.doff);
   EncArgs E = A;
   E.choices = nullptr;
   E.out = nullptr;
   E.copies = 0;
   E.rec = rec;
-  E.d_out = dblk;
-  int rc = launch_quantize_t<F>(E, RECORDS, stream);
+  if (launch_quantize_t<F>(E, RECORDS, qws, nullptr, nullptr, stream) != 0) return -1;
   hipLaunchKernelGGL(damping_kernel, dim3(static_cast<unsigned>((nl + 255) / 256)), dim3(256), 0, stream, hess, nl,
                      perc_damp, lam);
+  if (!launched_ok()) return -1;
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb;
   hipLaunchKernelGGL(choice_search_kernel<F>, dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::UNITS), 0,
-                     stream, A, static_cast<const uint32_t *>(rec), static_cast<const uint16_t *>(dblk), hess,
-                     static_cast<const float *>(lam), choices);
-  const hipError_t le = hipGetLastError();
-  hipFreeAsync(scratch, stream);
-  return (rc == 0 && le == hipSuccess) ? 0 : -1;
+                     stream, A, static_cast<const uint32_t *>(rec), dblk, hess, static_cast<const float *>(lam),
+                     choices);
+  return launched_ok() ? 0 : -1;
 }
 
-int launch_choice_search(int fmt, EncArgs A, const float *hess, float perc_damp, uint8_t *choices,
+int launch_choice_search(int fmt, EncArgs A, const float *hess, float perc_damp, uint8_t *choices, void *ws,
                          hipStream_t stream) {
   switch (fmt) {
-    case IQ2_XXS: return launch_choice_search_t<IQ2_XXS>(A, hess, perc_damp, choices, stream);
-    case IQ2_XS: return launch_choice_search_t<IQ2_XS>(A, hess, perc_damp, choices, stream);
-    case IQ2_S: return launch_choice_search_t<IQ2_S>(A, hess, perc_damp, choices, stream);
-    case IQ1_S: return launch_choice_search_t<IQ1_S>(A, hess, perc_damp, choices, stream);
-    case IQ1_M: return launch_choice_search_t<IQ1_M>(A, hess, perc_damp, choices, stream);
+    case IQ2_XXS: return launch_choice_search_t<IQ2_XXS>(A, hess, perc_damp, choices, ws, stream);
+    case IQ2_XS: return launch_choice_search_t<IQ2_XS>(A, hess, perc_damp, choices, ws, stream);
+    case IQ2_S: return launch_choice_search_t<IQ2_S>(A, hess, perc_damp, choices, ws, stream);
+    case IQ1_S: return launch_choice_search_t<IQ1_S>(A, hess, perc_damp, choices, ws, stream);
+    case IQ1_M: return launch_choice_search_t<IQ1_M>(A, hess, perc_damp, choices, ws, stream);
   }
   return -1;
 }

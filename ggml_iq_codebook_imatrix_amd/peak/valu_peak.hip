@@ -105,3 +105,38 @@ extern "C" int valu_peak(int mode, int iters, double *ops_per_s, double *instr_p
                                           : 0.0;
   return 0;
 }
+
+namespace {
+// One wave reads the shader clock counter and the constant-rate wall counter
+// across a fixed stretch of wall time.
+__global__ void clock_kernel(unsigned long long wall_ticks, unsigned long long *clocks) {
+  const unsigned long long c0 = clock64(), w0 = wall_clock64();
+  unsigned long long w = w0;
+  while (w - w0 < wall_ticks) w = wall_clock64();
+  if (threadIdx.x == 0) {
+    clocks[0] = clock64() - c0;
+    clocks[1] = w - w0;
+  }
+}
+}  // namespace
+
+// clock_hz: the shader clock over `us` microseconds of a one-wave kernel
+// launched on the null stream now (so it reads the clock the chip runs at
+// right after the work queued before it).  Returns 0, or -1 on a HIP error.
+extern "C" int shader_clock(int us, double *clock_hz) {
+  if (us < 1 || !clock_hz) return -1;
+  int dev = 0, wall_khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev);
+  if (wall_khz <= 0) return -1;
+  unsigned long long *clk = nullptr;
+  if (hipMalloc(&clk, 2 * sizeof(unsigned long long)) != hipSuccess) return -1;
+  const unsigned long long ticks = static_cast<unsigned long long>(wall_khz) * us / 1000;
+  hipLaunchKernelGGL(clock_kernel, dim3(1), dim3(64), 0, 0, ticks, clk);
+  unsigned long long c[2] = {0, 0};
+  const bool ok = hipGetLastError() == hipSuccess && hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost) == hipSuccess;
+  hipFree(clk);
+  if (!ok || c[1] == 0) return -1;
+  *clock_hz = static_cast<double>(c[0]) / (static_cast<double>(c[1]) / (wall_khz * 1e3));
+  return 0;
+}

@@ -6,17 +6,24 @@
  * Conventions for every entry point
  *  - Pointers marked (device) must point to device memory of the current HIP
  *    device; (host) pointers to host memory.  The caller owns every buffer.
+ *  - The library allocates no memory and keeps no state between calls (the
+ *    one exception, iq_quantize_noalloc, says so).  Calls that need scratch
+ *    take a caller-owned device workspace: `*_workspace_size` returns its size
+ *    in bytes for the call's sizes (0: none needed, workspace may be NULL);
+ *    any alignment is accepted.  The workspace is overwritten; it must not be
+ *    used by another call while this call's work is in flight.
  *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
  *    a return of IQ_OK means "validated and enqueued", not "finished".
- *  - A negative return is a host-detected error: nothing was enqueued and no
- *    output was touched.
+ *  - Every return code except IQ_ERR_HIP is host-detected before anything is
+ *    enqueued: no kernel ran and no output or workspace byte was touched.
+ *    IQ_ERR_HIP means a kernel launch failed: the kernels of this call before
+ *    it may already be enqueued (outputs and workspace then hold partial
+ *    results), nothing after it is.
  *  - Problems only the device can see (non-finite data, out-of-range fixed
  *    choices or expert ids, fp16 overflow of a block scale) are OR-ed into
  *    *status (device, int32, optional) as IQ_STATUS_* bits; the caller reads it
  *    after synchronising.  The library never synchronises the stream itself.
  *  - Dense tensors are row-major and contiguous.  Sizes are in elements.
- *  - Calls may allocate stream-ordered scratch (hipMallocAsync/hipFreeAsync on
- *    `stream`); IQ_ERR_HIP reports a failed allocation or launch.
  *
  * Sources are cited by page title and section:
  *  [2735]     "Add imatrix calibration for the GGML formats and use it for fused
@@ -31,6 +38,7 @@
 #ifndef IQ_H
 #define IQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -51,7 +59,7 @@ typedef enum {
 
 typedef enum { IQ_DTYPE_F32 = 0, IQ_DTYPE_BF16 = 1 } iq_dtype;
 
-/* Return codes (host-detected; nothing enqueued). */
+/* Return codes (all but IQ_ERR_HIP host-detected: nothing enqueued). */
 #define IQ_OK 0
 #define IQ_ERR_FMT (-1)    /* unknown format                                  */
 #define IQ_ERR_DTYPE (-2)  /* unknown dtype                                   */
@@ -60,13 +68,15 @@ typedef enum { IQ_DTYPE_F32 = 0, IQ_DTYPE_BF16 = 1 } iq_dtype;
                               the call then enqueues nothing and returns IQ_OK) */
 #define IQ_ERR_SHAPE (-4)  /* cols % 256 != 0, rows % rows_per_expert != 0, ... */
 #define IQ_ERR_ARG (-5)    /* other invalid argument (top_k, chunk_rows, ...)   */
-#define IQ_ERR_HIP (-6)    /* HIP allocation or launch failure                */
+#define IQ_ERR_HIP (-6)    /* a kernel launch failed (see the conventions)    */
+#define IQ_ERR_WORKSPACE (-7) /* workspace smaller than its size query returns */
 
 /* Device status bits, OR-ed into *status. */
 #define IQ_STATUS_NONFINITE 1  /* non-finite weight (block encoded as zeros) or activation */
 #define IQ_STATUS_OVERFLOW 2   /* fp16 block scale overflowed (block encoded as zeros)    */
 #define IQ_STATUS_BADCHOICE 4  /* fixed choice >= num_choices (block encoded as zeros)    */
-#define IQ_STATUS_BADIMP 8     /* importance non-finite or negative (block zeros / expert flat) */
+#define IQ_STATUS_BADIMP 8     /* importance outside [0, 2^64] (block zeros) or a non-finite /
+                                  negative statistic (expert flat)                          */
 #define IQ_STATUS_BADID 16     /* routed expert id outside [0, num_experts) (pair skipped) */
 
 /* Geometry of one layout ([3157]: each format records choice_groups and
@@ -101,14 +111,26 @@ int iq_format_info(int fmt, iq_format_info_t *out);
  *           one token counts per occurrence).
  *  counts   (device) [num_experts] int64, ACCUMULATED: counts[e] += number of
  *           such pairs (dense: += T).
+ *  workspace, workspace_bytes  (device) scratch of at least
+ *           iq_imatrix_collect_workspace_size(T, K, ids ? top_k : 0, num_experts,
+ *           chunk_rows) bytes.  Chunks are reduced in windows of several
+ *           chunks, so the size is bounded independently of T (slice partials
+ *           of one window, and for routed tokens its routing bitmaps).
  *  status   (device, nullable): IQ_STATUS_NONFINITE when a row that reached an
  *           expert holds a non-finite value (only touched experts are checked);
  *           IQ_STATUS_BADID for ids outside [0, num_experts) (those pairs skip).
- * Errors: IQ_ERR_NULL (x, sums, counts), IQ_ERR_DTYPE, IQ_ERR_ARG (T < 0,
- * K <= 0, top_k < 1 with ids, num_experts < 1, chunk_rows < 1). */
+ * Errors: IQ_ERR_NULL (x, sums, counts, or a needed workspace), IQ_ERR_DTYPE,
+ * IQ_ERR_ARG (T < 0, K <= 0, top_k < 1 with ids, num_experts < 1,
+ * chunk_rows < 1, sizes whose launches would not fit a grid),
+ * IQ_ERR_WORKSPACE, IQ_ERR_HIP. */
 int iq_imatrix_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids,
                        int top_k, int num_experts, int chunk_rows, float *sums, int64_t *counts,
-                       int32_t *status, hipStream_t stream);
+                       void *workspace, size_t workspace_bytes, int32_t *status, hipStream_t stream);
+
+/* Workspace bytes iq_imatrix_collect needs; top_k = 0 for a dense
+ * collection (ids NULL).  *bytes (host).  Errors: IQ_ERR_NULL, IQ_ERR_ARG. */
+int iq_imatrix_collect_workspace_size(int64_t T, int64_t K, int top_k, int num_experts, int chunk_rows,
+                                      size_t *bytes);
 
 /* Merge of two collections' statistics ([coverage] Facts: the GGUF imatrix
  * format stores in_sum2 and counts per tensor so that files can be merged;
@@ -135,10 +157,10 @@ int iq_imatrix_merge(const float *src_sums, const int64_t *src_counts, int num_e
  * floor"); [coverage] Facts: counts[e] == 0 gives weight 1 on every channel).
  *
  *  importance[e][j] = sqrt(max(m_j, floor_rel * mean_j m_j)), m_j = sums[e][j] /
- *  counts[e] (fp32, IEEE division and square root).  The mean is the exact
- *  fixed-point sum defined in iq_imatrix_importance's kernel comment, so it is
- *  reproducible bit for bit.  Experts with counts 0, an all-zero statistic, or
- *  a non-finite / negative m_j (IQ_STATUS_BADIMP) get all ones.
+ *  counts[e] (fp32, IEEE division and square root).  The mean is the plain
+ *  one: the m_j added in fp64 in ascending j, divided by K in fp64, rounded to
+ *  fp32.  Experts with counts 0, a mean that is 0, or a non-finite / negative
+ *  m_j (IQ_STATUS_BADIMP) get all ones.
  *  sums (device) [E, K] f32; counts (device) [E] int64; importance (device)
  *  [E, K] f32 (may alias nothing).  floor_rel: 1e-6 is the default used here.
  * Errors: IQ_ERR_NULL, IQ_ERR_ARG (E < 1, K <= 0, floor_rel < 0 or not finite). */
@@ -167,17 +189,42 @@ int iq_imatrix_importance(const float *sums, const int64_t *counts, int num_expe
  *              or NULL to search them.  IQ2: local scale in [0,16); IQ1_S:
  *              (delta_sign << 3) | local scale; IQ1_M: local scale in [0,8).
  *  out         (device) [rows, cols/256, block_bytes] uint8 payload.
+ *  workspace, workspace_bytes  (device) scratch of at least
+ *              iq_quantize_workspace_size(fmt, rows, cols, rows_per_expert,
+ *              importance != NULL) bytes: the weighted norms of every grid entry
+ *              per (expert, 8-column group), the fp16 block scales and the
+ *              importance flags.
  *  status      (device, nullable) IQ_STATUS_* bits.
- * Every block is written; a block holding a non-finite value, a bad
- * importance value, an out-of-range choice, an fp16-overflowing scale, or only
- * zeros is written as all-zero bytes ([3157] review: all-zero block -> all-zero
- * payload).
- * Errors: IQ_ERR_FMT, IQ_ERR_DTYPE, IQ_ERR_NULL (w, grid, out), IQ_ERR_SHAPE
- * (rows < 0, cols <= 0 or % 256, rows_per_expert < 1 or not dividing rows),
- * IQ_ERR_HIP. */
+ * Every block is written; a block holding a non-finite value, an importance
+ * value outside [0, 2^64], an out-of-range choice, an fp16-overflowing scale,
+ * or only zeros is written as all-zero bytes ([3157] review: all-zero block ->
+ * all-zero payload).  The grid's values are taken to lie in the layout's
+ * alphabet range (IQ2 magnitudes in [0, 5], IQ1 values in [-1, 1]), which the
+ * scale anchor assumes.
+ * Errors: IQ_ERR_FMT, IQ_ERR_DTYPE, IQ_ERR_NULL (w, grid, out, or a needed
+ * workspace), IQ_ERR_SHAPE (rows < 0, cols <= 0 or % 256, rows_per_expert < 1
+ * or not dividing rows, sizes whose launches would not fit a grid),
+ * IQ_ERR_WORKSPACE, IQ_ERR_HIP. */
 int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
                 int64_t rows_per_expert, const float *grid, const float *importance,
-                const uint8_t *choices, uint8_t *out, int32_t *status, hipStream_t stream);
+                const uint8_t *choices, uint8_t *out, void *workspace, size_t workspace_bytes,
+                int32_t *status, hipStream_t stream);
+
+/* Workspace bytes iq_quantize and iq_quantize_every_choice need (weighted:
+ * importance given).  *bytes (host).  Errors: IQ_ERR_FMT, IQ_ERR_NULL,
+ * IQ_ERR_SHAPE. */
+int iq_quantize_workspace_size(int fmt, int64_t rows, int64_t cols, int64_t rows_per_expert, int weighted,
+                               size_t *bytes);
+
+/* iq_quantize, also recording `search_start` on `stream` just before its
+ * search kernel and `search_stop` just after it, so hipEventElapsedTime gives
+ * that kernel's duration alone (a measurement aid, not part of the method).
+ * Both events must have been created on the current device.
+ * Errors: as iq_quantize, plus IQ_ERR_NULL for a NULL event. */
+int iq_quantize_timed(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
+                      int64_t rows_per_expert, const float *grid, const float *importance,
+                      const uint8_t *choices, uint8_t *out, void *workspace, size_t workspace_bytes,
+                      int32_t *status, hipEvent_t search_start, hipEvent_t search_stop, hipStream_t stream);
 
 /* Every-choice encode ([3157] series, squashed #3159 "one-pass every-choice
  * encode": each 256-column block encoded under every choice from a single
@@ -185,10 +232,12 @@ int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
  *  out (device) [num_choices, rows, cols/256, block_bytes]: out[c] is exactly
  *  the payload iq_quantize writes with `choices` set to c for every unit
  *  (IQ1_S: c = (delta_sign << 3) | local scale).
- *  Other arguments, status bits and errors as iq_quantize (no `choices`). */
+ *  Other arguments, the workspace (iq_quantize_workspace_size), status bits
+ *  and errors as iq_quantize (no `choices`). */
 int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
                              int64_t rows_per_expert, const float *grid, const float *importance,
-                             uint8_t *out, int32_t *status, hipStream_t stream);
+                             uint8_t *out, void *workspace, size_t workspace_bytes, int32_t *status,
+                             hipStream_t stream);
 
 /* Local-Hessian choice search ([3157] series, squashed #3158 "local_hessian
  * for GGML IQ": encode each block under every choice; give each choice unit its
@@ -204,6 +253,10 @@ int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, in
  *           given, the payload under the picks -- byte for byte what iq_quantize
  *           writes with `choices` -- packed from the every-choice fields the
  *           search already holds, so no second sweep is needed.
+ *  workspace, workspace_bytes  (device) scratch of at least
+ *           iq_choice_search_workspace_size(...) bytes: every group's fields
+ *           under every choice (num_choices * rows * cols/8 * 4 bytes), the
+ *           damping terms and an encoder workspace.
  *  importance, grid, w, rows_per_expert, status: as iq_quantize (the codebook
  *  search keeps the importance weighting).
  * Errors: as iq_quantize, plus IQ_ERR_NULL (hess, choices) and IQ_ERR_ARG
@@ -211,7 +264,12 @@ int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, in
 int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
                      int64_t rows_per_expert, const float *grid, const float *importance,
                      const float *hess, float perc_damp, uint8_t *choices, uint8_t *out,
-                     int32_t *status, hipStream_t stream);
+                     void *workspace, size_t workspace_bytes, int32_t *status, hipStream_t stream);
+
+/* Workspace bytes iq_choice_search needs (weighted: importance given).
+ * Errors: IQ_ERR_FMT, IQ_ERR_NULL, IQ_ERR_SHAPE. */
+int iq_choice_search_workspace_size(int fmt, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                                    int weighted, size_t *bytes);
 
 /* Hessian diagonal blocks for iq_choice_search ([3157] series, squashed #3158
  * "local_hessian for GGML IQ": the layer-output error is measured under the
@@ -229,6 +287,10 @@ int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t co
  *           by T, top_k and K (256 to 1,024 entries, more if the partial blocks
  *           would pass 512 MiB), else taken whole.  Partial blocks are added in
  *           split order, so results repeat bit for bit.
+ *  workspace, workspace_bytes  (device) scratch of at least
+ *           iq_hessian_collect_workspace_size(T, K, ids ? top_k : 0,
+ *           num_experts, chunk_rows) bytes: split partial blocks (at most
+ *           512 MiB for routed tokens) and, routed, the token lists.
  *  status   (device, nullable): IQ_STATUS_NONFINITE when a token that reached an
  *           expert holds a non-finite value; IQ_STATUS_BADID as
  *           iq_imatrix_collect.
@@ -236,7 +298,13 @@ int iq_choice_search(int fmt, const void *w, int dtype, int64_t rows, int64_t co
  * multiple of 256) and IQ_ERR_ARG (num_experts * K above 2^30, T of 2^31 or
  * more). */
 int iq_hessian_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t *ids, int top_k,
-                       int num_experts, int chunk_rows, float *hess, int32_t *status, hipStream_t stream);
+                       int num_experts, int chunk_rows, float *hess, void *workspace, size_t workspace_bytes,
+                       int32_t *status, hipStream_t stream);
+
+/* Workspace bytes iq_hessian_collect needs; top_k = 0 for dense tokens.
+ * Errors: IQ_ERR_NULL, IQ_ERR_ARG, IQ_ERR_SHAPE. */
+int iq_hessian_collect_workspace_size(int64_t T, int64_t K, int top_k, int num_experts, int chunk_rows,
+                                      size_t *bytes);
 
 /* Decode ([2513]: dequantize_row semantics; IQ1_M d reassembled from the top
  * nibbles of the four scale words, one 3-bit scale per two groups).
@@ -247,14 +315,6 @@ int iq_hessian_collect(const void *x, int dtype, int64_t T, int64_t K, const int
  * Errors: IQ_ERR_FMT, IQ_ERR_DTYPE, IQ_ERR_NULL, IQ_ERR_SHAPE. */
 int iq_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, const float *grid,
                   void *out, int dtype, hipStream_t stream);
-
-/* Profiling hook (not part of the method): the next iq_quantize call made on
- * the calling host thread records `start` on its stream just before its search
- * kernel and `stop` just after it, so hipEventElapsedTime gives that kernel's
- * duration alone; the hook then clears itself.  Both events must be created
- * by the caller on the current device, or both NULL to clear.
- * Errors: IQ_ERR_NULL when exactly one event is NULL. */
-int iq_time_next_search(hipEvent_t start, hipEvent_t stop);
 
 /* Short text for a return code (static storage). */
 const char *iq_error_string(int code);

@@ -48,6 +48,11 @@
  *  R12 the reduced error: per group t = s*G - 2P, G = sum a_j u_j^2,
  *      P = sum a_j y_j u_j, computed as written in iq2_group/iq1_group.
  *  R13 byte layouts (sizes fixed by [2513]; field positions our own).
+ *  R20 a block whose importance holds a value outside [0, 2^64] (NaN, a
+ *      negative value, or one no floored square root of a finite fp32 second
+ *      moment can reach, since sqrt(FLT_MAX) < 2^64) is refused: all-zero
+ *      bytes and the BADIMP status bit.  Within that range and with a finite
+ *      fp16 scale every fp32 intermediate of the search stays finite.
  */
 #include <math.h>
 #include <stdint.h>
@@ -63,6 +68,9 @@ enum { ORC_IQ2_XXS = 0, ORC_IQ2_XS = 1, ORC_IQ2_S = 2, ORC_IQ1_S = 3, ORC_IQ1_M 
 #define ORC_ST_BADCHOICE 4
 #define ORC_ST_BADIMP 8
 #define ORC_ST_BADID 16
+
+/* largest accepted importance value (R20): 2^64 */
+#define ORC_IMP_MAX 18446744073709551616.0f
 
 typedef struct {
   int block_bytes; /* [2513]: 2.0625 / 2.3125 / 2.5625 / 1.5625 / 1.75 bits per weight */
@@ -575,8 +583,8 @@ static int encode_block(int fmt, const float *x, const float *a, const float *gr
   int st = 0;
   uint16_t d16;
   int bad_imp = 0;
-  for (int j = 0; j < 256; ++j)
-    if (!isfinite(a[j]) || a[j] < 0.0f) bad_imp = 1;
+  for (int j = 0; j < 256; ++j) /* R20: usable weights lie in [0, 2^64] */
+    if (!(a[j] >= 0.0f && a[j] <= ORC_IMP_MAX)) bad_imp = 1;
   if (d16_override >= 0) {
     d16 = (uint16_t)d16_override;
     for (int j = 0; j < 256; ++j)

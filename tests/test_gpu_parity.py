@@ -456,6 +456,94 @@ def test_importance_parity(api, orc):
     assert np.all(got[1] == 1.0) and np.all(got[4] == 1.0) and np.all(got[6] == 1.0)
 
 
+def test_importance_mean_is_the_sequential_fp64_mean(api, orc):
+    """The floor's mean on the device is the running fp64 sum in ascending j:
+    floor_rel = 1 makes every value below the mean take sqrt(mean) exactly, so
+    the mean's fp32 bits show.  Wide-range statistics (lognormal(0, 6)) at
+    several widths, plus a hand case whose sequential mean is an fp32 midpoint
+    (0.5 + 2^-25, rounding to 0.5) while the exact or pairwise mean rounds up."""
+    say("importance sequential mean")
+    g = inputs.rng(1710)
+    for K in (1, 63, 64, 65, 2048, 5000, 17408):
+        E = 3
+        sums = g.lognormal(0, 6, (E, K)).astype(np.float32)
+        sums[:, g.random(K) < 0.1] = 0.0
+        counts = np.array([1, 3, 977], np.int64)
+        for fl in (1e-6, 1.0):
+            got = host(api.imatrix_importance(dev(sums), dev(counts), fl))
+            want, _ = orc.importance(sums, counts, fl)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (K, fl)
+    hand = np.array([[4.0, 2.0 ** -22] + [2.0 ** -52] * 6], np.float32)
+    got = host(api.imatrix_importance(dev(hand), dev(np.array([1], np.int64)), 1.0))
+    assert got[0, 2] == np.sqrt(np.float32(0.5))
+    want, _ = orc.importance(hand, np.array([1], np.int64), 1.0)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_importance_range_edges(api, orc, fmt):
+    """Importance up to 2^64 (scaled so its maximum is 2^64) with a block at the
+    largest amax whose fp16 scale is finite: the payload equals the one at the
+    unscaled importance, on the device as in the oracle; a value above 2^64
+    refuses its block with the BADIMP bit."""
+    say("importance range", fmt)
+    grid = inputs.grid_for(fmt, 3603)
+    w = inputs.weight(70, 512, 3600, 3601, bf16=False)
+    w[0, :256] *= np.float32(1.0e6 / np.abs(w[0, :256]).max())
+    imp = inputs.importance_like(512, 3602)
+    big = (imp * np.float32(2.0 ** (64 - np.ceil(np.log2(imp.max()))))).astype(np.float32)
+    bad = big.copy()
+    bad[300] = np.float32(2.0 ** 65)
+    base, _ = run_encode(api, fmt, w, "f32", grid, imp[None])
+    for a, st_want in ((big, 0), (bad, 8)):
+        got, st = run_encode(api, fmt, w, "f32", grid, a[None])
+        want, st_o = orc.quantize(fmt, w, grid, a[None])
+        assert st == st_o == st_want
+        assert np.array_equal(got, want)
+    assert np.array_equal(run_encode(api, fmt, w, "f32", grid, big[None])[0], base)
+
+
+@pytest.mark.parametrize("routed", [False, True])
+def test_collect_windows(api, orc, routed):
+    """Collections longer than one window of chunks (the workspace holds one
+    window's partials): counts exact, sums within 1e-5 of the oracle's fp64
+    sums, and the workspace does not grow with the token count."""
+    say("collect windows", routed)
+    if routed:
+        T, K, E, top_k, chunk = 2000, 2048, 128, 4, 100     # windows of 8 chunks of 100 tokens
+        ids = inputs.routing(T, top_k, E, 1781, n_idle=5)
+    else:
+        T, K, E, top_k, chunk = 2649, 4096, 1, 0, 2       # windows of 512 two-token chunks
+        ids = None
+    x = inputs.activations(T, K, 1782, 1783, bf16=True)
+    ws_small = api.collect_workspace_size(T, K, top_k, E, chunk)
+    assert ws_small == api.collect_workspace_size(50 * T, K, top_k, E, chunk)
+    sums, counts = api.imatrix_collect(dev_w(x, "bf16"), None if ids is None else dev(ids), E, chunk_rows=chunk)
+    want, wc, _ = orc.collect(x, ids, E) if routed else orc.collect(x)
+    assert np.array_equal(host(counts), wc)
+    got = host(sums).astype(np.float64)
+    assert np.all(np.abs(got - want) <= 1e-5 * want)
+
+
+def test_workspace_reuse_and_alignment(api):
+    """A caller workspace at an odd byte offset, reused across formats and
+    calls of different sizes, gives the same payloads as fresh ones."""
+    say("workspace reuse")
+    w = dev_w(inputs.weight(200, 1024, 1790, 1791), "bf16")
+    imp = dev(inputs.importance_like(1024, 1792)[None, :])
+    need = max(api.quantize_workspace_size(f, 200, 1024) for f in FORMATS)
+    buf = torch.full((need + 3,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = buf[3:]
+    for f in FORMATS + FORMATS[::-1]:
+        g = dev(inputs.grid_for(f, GRID_SEED[f]))
+        for r in (200, 70):
+            a = host(api.quantize(f, w[:r], g, imp, workspace=ws))
+            b = host(api.quantize(f, w[:r], g, imp))
+            assert np.array_equal(a, b), (f, r)
+    with pytest.raises(api.IQError):
+        api.quantize("IQ2_XS", w, dev(inputs.grid_for("IQ2_XS", 202)), imp, workspace=ws[:16])
+
+
 # ---------------------------------------------------------------------------
 # Hessian diagonal blocks (the input to the local-Hessian choice search).
 # Small-integer activations make every product and partial sum exact in fp32,

@@ -348,3 +348,27 @@ def test_zero_block_gives_zero_payload(orc, fmt):
     grid = inputs.grid_for(fmt, 201)
     out, st = orc.encode_block(fmt, np.zeros(256, np.float32), np.ones(256, np.float32), grid)
     assert st == 0 and not out.any()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_importance_range_and_power_of_two_scaling(orc, fmt):
+    """R20: importance values up to 2^64 are accepted.  Scaling every weight by
+    a power of two scales every fp32 step of the search exactly unless a value
+    overflows, so the payload at importance scaled to a maximum of 2^64 -- with
+    one block at the largest amax whose fp16 scale is finite -- equals the
+    payload at the unscaled importance.  A value above 2^64 refuses its block."""
+    grid = inputs.grid_for(fmt, 3603)
+    w = inputs.weight(4, 512, 3600, 3601, bf16=False)
+    w[0, :256] *= np.float32(1.0e6 / np.abs(w[0, :256]).max())
+    imp = inputs.importance_like(512, 3602)
+    big = (imp * np.float32(2.0 ** (64 - np.ceil(np.log2(imp.max()))))).astype(np.float32)
+    assert big.max() <= 2.0 ** 64 and big.max() >= 2.0 ** 63
+    p1, st1 = orc.quantize(fmt, w, grid, imp[None])
+    p2, st2 = orc.quantize(fmt, w, grid, big[None])
+    assert st1 == st2 == 0 and p1[0, 0].any()
+    assert np.array_equal(p1, p2)
+    bad = big.copy()
+    bad[300] = np.float32(2.0 ** 65)
+    p3, st3 = orc.quantize(fmt, w, grid, bad[None])
+    assert st3 & orc.ST_BADIMP
+    assert not p3[:, 1].any() and np.array_equal(p3[:, 0], p1[:, 0])
