@@ -37,6 +37,7 @@ SIGNATURES = {
     "iq_imatrix_importance": ([_P, _P, _I, _I64, _F, _P, _P, _P], _I),
     "iq_quantize_workspace_size": ([_I, _I64, _I64, _I64, _I, _P], _I),
     "iq_quantize": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P, _P], _I),
+    "iq_quantize_noalloc": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
     "iq_quantize_timed": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P], _I),
     "iq_quantize_every_choice": ([_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P, _P], _I),
     "iq_choice_search_workspace_size": ([_I, _I64, _I64, _I64, _I, _P], _I),
@@ -352,6 +353,32 @@ def quantize(fmt, w: torch.Tensor, grid: torch.Tensor, importance: torch.Tensor 
         st = read_status(status)
         if st:
             raise IQError(f"iq_quantize device status {st:#x}")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # IQ_NOALLOC_SCRATCH_BYTES
+
+
+def quantize_noalloc(fmt, w: torch.Tensor, grid: torch.Tensor, importance: torch.Tensor | None = None,
+                     rows_per_expert: int | None = None, choices: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, status: torch.Tensor | None = None) -> torch.Tensor:
+    """quantize() through iq_quantize_noalloc: the library works in its static
+    device scratch, so apart from `out` when it is not given nothing is
+    allocated.  Calls that overlap on one GPU race (they share the scratch)."""
+    f, rows, cols, rpe, info = _encode_args(fmt, w, grid, importance, rows_per_expert)
+    nb = cols // 256
+    if choices is not None:
+        _need(choices, "choices", (rows, nb, info["choice_groups"]), torch.uint8)
+    if out is not None:
+        _need(out, "out", (rows, nb, info["block_bytes"]), torch.uint8)
+    _status_ok(status)
+    dev = _device_of(w)
+    if out is None:
+        out = torch.empty((rows, nb, info["block_bytes"]), dtype=torch.uint8, device=dev)
+    rc = lib().iq_quantize_noalloc(f, _ptr(w, "w", dev), DTYPE[w.dtype], rows, cols, rpe, _ptr(grid, "grid", dev),
+                                   _ptr(importance, "importance", dev), _ptr(choices, "choices", dev),
+                                   _ptr(out, "out", dev), _ptr(status, "status", dev), _stream())
+    _check(rc, "iq_quantize_noalloc")
     return out
 
 

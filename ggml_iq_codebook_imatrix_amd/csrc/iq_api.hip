@@ -3,11 +3,40 @@
 // device memory or synchronises the stream; every size a launch depends on is
 // checked before the first kernel is enqueued.
 
+#include <atomic>
+#include <mutex>
+
 #include "iq.h"
 #include "iq_common.hpp"
 #include "iq_internal.hpp"
 
+// Scratch of iq_quantize_noalloc, for callers that cannot allocate.  Each
+// device the library runs on holds its own copy until the process ends.  Host
+// code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[IQ_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_dev[kMaxDevices];  // device address of `scratch` per device, once known
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (nullptr on a HIP error).
+void *noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_dev[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 struct FmtRow {
   int block_bytes, grid_size, choice_groups, num_choices, groups_per_choice;
@@ -231,6 +260,24 @@ int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, i
                 size_t workspace_bytes, int32_t *status, hipStream_t stream) {
   return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, choices, out, workspace,
                          workspace_bytes, status, false, nullptr, nullptr, stream);
+}
+
+int iq_quantize_noalloc(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,
+                        const float *grid, const float *importance, const uint8_t *choices, uint8_t *out,
+                        int32_t *status, hipStream_t stream) {
+  // the host checks of iq_quantize first, so a bad call never touches HIP
+  if (bad_fmt(fmt)) return IQ_ERR_FMT;
+  if (bad_dtype(dtype)) return IQ_ERR_DTYPE;
+  if (!grid || (rows != 0 && (!w || !out))) return IQ_ERR_NULL;
+  const int rc = check_encode_shape(rows, cols, rows_per_expert, fmt, wg_cols(fmt));
+  if (rc != IQ_OK) return rc;
+  if (rows == 0) return IQ_OK;
+  if (iq::plan_quantize(fmt, rows, cols, rows_per_expert, importance != nullptr).bytes > IQ_NOALLOC_SCRATCH_BYTES)
+    return IQ_ERR_WORKSPACE;
+  void *ws = noalloc_scratch();
+  if (!ws) return IQ_ERR_HIP;
+  return quantize_common(fmt, w, dtype, rows, cols, rows_per_expert, grid, importance, choices, out, ws,
+                         IQ_NOALLOC_SCRATCH_BYTES, status, false, nullptr, nullptr, stream);
 }
 
 int iq_quantize_timed(int fmt, const void *w, int dtype, int64_t rows, int64_t cols, int64_t rows_per_expert,

@@ -216,6 +216,27 @@ int iq_quantize(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
 int iq_quantize_workspace_size(int fmt, int64_t rows, int64_t cols, int64_t rows_per_expert, int weighted,
                                size_t *bytes);
 
+/* Bytes of the static device scratch iq_quantize_noalloc works in (64 MiB). */
+#define IQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* iq_quantize for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid it): same
+ * arguments, results and errors as iq_quantize, without a workspace.  Its
+ * scratch is a static device array of IQ_NOALLOC_SCRATCH_BYTES that each GPU
+ * the library runs on holds until the process ends; the first call on a
+ * device looks up that device's address (hipGetSymbolAddress), and no call
+ * allocates or frees anything.  Every call on a device shares its array and
+ * leaves it holding that call's scratch, so calls that overlap on one GPU
+ * (other streams, other threads) race: serialise them.
+ * Limit: iq_quantize_workspace_size(fmt, rows, cols, rows_per_expert,
+ * importance != NULL) must not exceed IQ_NOALLOC_SCRATCH_BYTES -- e.g. any
+ * dense weight up to 17408 x 5120, or 128 experts x 2048 columns in the
+ * IQ2 layouts -- else IQ_ERR_WORKSPACE before anything is enqueued.
+ * IQ_ERR_HIP also reports a failed address lookup. */
+int iq_quantize_noalloc(int fmt, const void *w, int dtype, int64_t rows, int64_t cols,
+                        int64_t rows_per_expert, const float *grid, const float *importance,
+                        const uint8_t *choices, uint8_t *out, int32_t *status, hipStream_t stream);
+
 /* iq_quantize, also recording `search_start` on `stream` just before its
  * search kernel and `search_stop` just after it, so hipEventElapsedTime gives
  * that kernel's duration alone (a measurement aid, not part of the method).

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["iq_format_info", "iq_imatrix_collect", "iq_imatrix_collect_workspace_size", "iq_hessian_collect",
          "iq_hessian_collect_workspace_size", "iq_imatrix_merge", "iq_imatrix_importance", "iq_quantize",
-         "iq_quantize_workspace_size", "iq_quantize_timed", "iq_quantize_every_choice", "iq_choice_search",
+         "iq_quantize_workspace_size", "iq_quantize_noalloc", "iq_quantize_timed", "iq_quantize_every_choice", "iq_choice_search",
          "iq_choice_search_workspace_size", "iq_dequantize", "iq_error_string"])
 
 
