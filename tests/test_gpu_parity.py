@@ -5,6 +5,8 @@ the fp64 oracle; importance bit-exact from the same fp32 sums; decoded values
 bit-exact (fp32) / round-to-nearest-even of the oracle's (bf16).  Encode parity
 feeds the same importance array to both sides.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -19,6 +21,23 @@ GRID_SEED = {"IQ2_XXS": 201, "IQ2_XS": 202, "IQ2_S": 203, "IQ1_S": 204, "IQ1_M":
 
 def say(*a):
     print("[case]", *a, flush=True)
+
+
+# Full-size configurations are checked against the oracle on a seeded subset of
+# SAMPLE_ROWS rows that always holds the last row (and any rows a test adds);
+# with IQ_FULL_PARITY=1 in the environment every row is checked instead.
+SAMPLE_ROWS = 1024
+FULL = os.environ.get("IQ_FULL_PARITY") == "1"
+THREADS = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+
+def sample_rows(n, seed, extra=()):
+    """Sorted row ids: SAMPLE_ROWS seeded rows of n (every row when IQ_FULL_PARITY
+    is set or n is small), the last row and `extra` always included."""
+    if FULL or n <= SAMPLE_ROWS:
+        return np.arange(n)
+    rid = inputs.rng(seed).choice(n - 1, SAMPLE_ROWS - 1 - len(extra), replace=False)
+    return np.unique(np.concatenate([rid, np.asarray(extra, np.int64), [n - 1]])).astype(np.int64)
 
 
 @pytest.fixture(scope="module")
@@ -170,9 +189,11 @@ def test_every_choice_full_size_sampled(api, orc):
     w, x, grid, spec = inputs.workload("iq2_xs_5632x2048")
     _, _, imp = _oracle_importance(orc, x)
     every = host(api.quantize_every_choice("IQ2_XS", dev_w(w, "bf16"), dev(grid), dev(imp)))
-    rid = np.sort(inputs.rng(2200).choice(w.shape[0], 12, replace=False))
-    want, _ = orc.quantize_every_choice("IQ2_XS", w, grid, imp, row_ids=rid)
-    assert np.array_equal(every[:, rid], want)
+    rid = sample_rows(w.shape[0], 2200)
+    want, _ = orc.quantize_every_choice("IQ2_XS", w, grid, imp, row_ids=rid, threads=THREADS)
+    for c in range(want.shape[0]):
+        bad = np.argwhere((every[c, rid] != want[c]).any(axis=-1))
+        assert bad.size == 0, f"choice {c}: {len(bad)} blocks differ, first {bad[:5].tolist()}"
 
 
 def _correlated_hessian(E, nb, T, seed):
@@ -221,6 +242,47 @@ def test_choice_search_parity(api, orc, fmt):
     assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
 
 
+def _adversarial_hessian(nb, seed):
+    """[1, nb, 256, 256] symmetric f32 blocks whose entries span 2^-60..2^60,
+    with rows of alternating-sign near-equal pairs (their products cancel in
+    the running sums), a share of subnormal entries (2^-149..2^-127) whose
+    products with the residuals underflow, and exact zeros."""
+    g = inputs.rng(seed)
+    out = np.empty((1, nb, 256, 256), np.float32)
+    for b in range(nb):
+        a = g.uniform(1, 2, (256, 256)) * np.exp2(g.integers(-60, 61, (256, 256))) * g.choice([-1, 1], (256, 256))
+        rows = g.choice(256, 64, replace=False)
+        a[rows, 0::2] = np.abs(a[rows, 0::2])
+        a[rows, 1::2] = -a[rows, 0::2] * (1 + np.exp2(-g.integers(8, 24, (64, 128))))
+        sub = g.random((256, 256)) < 0.05
+        a[sub] = g.uniform(1, 2, sub.sum()) * np.exp2(g.integers(-149, -127, sub.sum()))
+        a[g.random((256, 256)) < 0.02] = 0.0
+        a = np.triu(a) + np.triu(a, 1).T
+        np.fill_diagonal(a, np.abs(np.diag(a)))
+        out[0, b] = a.astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_choice_search_adversarial_hessian(api, orc, fmt):
+    """The Hessian products (matrix cores on the device, fmaf chains in the
+    oracle) on blocks spanning many binades, with cancelling rows and
+    subnormal entries and products: picks and payload bit-exact."""
+    say("choice search adversarial H", fmt)
+    grid = inputs.grid_for(fmt, GRID_SEED[fmt])
+    w = inputs.weight(70, 512, 2600, 2601, bf16=False)
+    hess = _adversarial_hessian(2, 2602)
+    imp = inputs.importance_like(512, 2603)[None, :]
+    st = api.new_status()
+    got, pay = api.choice_search(fmt, dev(w), dev(grid), dev(hess), dev(imp), status=st, payload=True)
+    want, st_o = orc.choice_search(fmt, w, grid, hess, imp)
+    assert int(host(st)[0]) == st_o == 0
+    bad = np.argwhere(host(got) != want)
+    assert bad.size == 0, f"{len(bad)} picks differ, first {bad[:5].tolist()}"
+    pw, _ = orc.quantize(fmt, w, grid, imp, choices=want)
+    assert np.array_equal(host(pay), pw)
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_choice_search_f32_flat(api, orc, fmt):
     """fp32 weights, flat importance, a ragged 64-row tile, one block column."""
@@ -250,12 +312,11 @@ def test_choice_search_full_size_sampled(api, orc, fmt):
     del hess64
     got, pay = api.choice_search(fmt, dev_w(w, "bf16"), dev(grid), dev(hess), dev(imp), payload=True)
     got, pay = host(got), host(pay)
-    rid = np.sort(inputs.rng(2400).choice(w.shape[0], 8, replace=False))
-    rid[-1] = w.shape[0] - 1
-    want, _ = orc.choice_search(fmt, w, grid, hess, imp, row_ids=rid, threads=16)
+    rid = sample_rows(w.shape[0], 2400)
+    want, _ = orc.choice_search(fmt, w, grid, hess, imp, row_ids=rid, threads=THREADS)
     bad = np.argwhere(got[rid] != want)
     assert bad.size == 0, f"{len(bad)} picks differ, first {bad[:5].tolist()}"
-    pw, _ = orc.quantize(fmt, w[rid], grid, imp, choices=want)
+    pw, _ = orc.quantize(fmt, w[rid], grid, imp, choices=want, threads=THREADS)
     assert np.array_equal(pay[rid], pw)
 
 
@@ -709,12 +770,11 @@ def test_workload_full_size(api, orc, name):
     imp = dev(imp_h)
     wd = dev_w(w, "bf16")
     got = host(api.quantize(fmt, wd, dev(grid), imp))
-    if fmt.startswith("IQ1"):  # sampled rows (the oracle's IQ1 search is ~10x the IQ2 cost)
-        rid = np.sort(inputs.rng(1800).choice(w.shape[0], 96, replace=False))
-        rid[-1] = w.shape[0] - 1
+    if fmt.startswith("IQ1"):  # sampled rows (the oracle's IQ1 search is ~4x the IQ2 cost)
+        rid = sample_rows(w.shape[0], 1800)
     else:                      # every row
         rid = np.arange(w.shape[0])
-    want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid, threads=16)
+    want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid, threads=THREADS)
     bad = np.argwhere((got[rid] != want).any(axis=2))
     assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
     # decoded importance-weighted error: the GPU's decode of its payload against
@@ -729,7 +789,7 @@ def test_workload_full_size(api, orc, name):
         geo = orc.geometry(fmt)
         ch = np.full((w.shape[0], w.shape[1] // 256, geo["units"]), 7, np.uint8)
         got7 = host(api.quantize(fmt, wd, dev(grid), imp, choices=dev(ch)))
-        want7, _ = orc.quantize(fmt, w, grid, imp_h, choices=ch, row_ids=rid)
+        want7, _ = orc.quantize(fmt, w, grid, imp_h, choices=ch, row_ids=rid, threads=THREADS)
         assert np.array_equal(got7[rid], want7)
 
 
@@ -742,9 +802,10 @@ def test_workload_iq1_17408x5120_sampled_rows(api, orc, fmt):
     s_o, c_o, imp_h = _oracle_importance(orc, x)
     _check_statistics(api, orc, sums, counts, s_o, c_o, imp_h)
     got = host(api.quantize(fmt, dev_w(w, "bf16"), dev(grid), dev(imp_h)))
-    rid = np.sort(inputs.rng(1850).choice(w.shape[0], 16, replace=False))
-    want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid, threads=16)
-    assert np.array_equal(got[rid], want)
+    rid = sample_rows(w.shape[0], 1850)
+    want, _ = orc.quantize(fmt, w, grid, imp_h, row_ids=rid, threads=THREADS)
+    bad = np.argwhere((got[rid] != want).any(axis=2))
+    assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
 
 
 def test_workload_moe_experts(api, orc):
@@ -761,8 +822,12 @@ def test_workload_moe_experts(api, orc):
     assert np.all(host(api.imatrix_importance(sums, counts))[c == 0] == 1.0)
     got = host(api.quantize("IQ2_XXS", dev_w(w, "bf16"), dev(grid), dev(imp_h), rows_per_expert=rpe))
     idle = np.flatnonzero(c == 0)
-    g = inputs.rng(1900)
-    rid = np.sort(np.concatenate([g.choice(w.shape[0], 40, replace=False), idle[:2] * rpe + 5,
-                                  [w.shape[0] - 1]]))
-    want, _ = orc.quantize("IQ2_XXS", w, grid, imp_h, rows_per_expert=rpe, row_ids=rid)
-    assert np.array_equal(got[rid], want)
+    # rows of every idle expert (first, a middle one, last) plus the seeded sample
+    extra = np.concatenate([[e * rpe, e * rpe + 5, e * rpe + rpe - 1] for e in idle])
+    rid = sample_rows(w.shape[0], 1900, extra)
+    want, _ = orc.quantize("IQ2_XXS", w, grid, imp_h, rows_per_expert=rpe, row_ids=rid, threads=THREADS)
+    bad = np.argwhere((got[rid] != want).any(axis=2))
+    assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
+    # idle experts take the flat search: their rows equal the unweighted encode
+    flat = host(api.quantize("IQ2_XXS", dev_w(w[idle[0] * rpe:(idle[0] + 1) * rpe], "bf16"), dev(grid)))
+    assert np.array_equal(got[idle[0] * rpe:(idle[0] + 1) * rpe], flat)
