@@ -207,8 +207,11 @@ def main() -> int:
     w = to_dev_bf16(w32)
     x = to_dev_bf16(x32)
     grid = torch.from_numpy(grid32).to(dev)
-    sums = torch.zeros((1, cols), dtype=torch.float32, device=dev)
-    counts = torch.zeros((1,), dtype=torch.int64, device=dev)
+    # the statistics accumulate, so each step clears them: one buffer holds
+    # sums [1, cols] f32 and counts [1] i64, cleared by one fill
+    acc = torch.zeros(cols * 4 + 8, dtype=torch.uint8, device=dev)
+    sums = acc[:cols * 4].view(torch.float32).view(1, cols)
+    counts = acc[cols * 4:].view(torch.int64)
     imp = torch.empty((1, cols), dtype=torch.float32, device=dev)
     packed = torch.empty((rows, cols // 256, api.format_info(fmt)["block_bytes"]), dtype=torch.uint8, device=dev)
     w_hat = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
@@ -222,8 +225,7 @@ def main() -> int:
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
     def step(i=None):
-        sums.zero_()
-        counts.zero_()
+        acc.zero_()
         api.imatrix_collect(x, chunk_rows=1024, sums=sums, counts=counts, status=status, workspace=ws_c)
         api.imatrix_importance(sums, counts, out=imp, status=status)
         api.quantize(fmt, w, grid, imp, out=packed, status=status, workspace=ws_q,

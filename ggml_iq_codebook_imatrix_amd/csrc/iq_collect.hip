@@ -334,18 +334,14 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
 // (IEEE fp32 division and square root).  The mean is the plain one: the m_j
 // added one after another in fp64, j ascending from 0, the total divided by K
 // in fp64 and rounded to fp32.  That running sum is one dependent chain: wave 0
-// walks it 64 values at a time (each lane converts one m_j, a lane read hands
-// it to the chain), prefetching the next 64 while it adds; the other waves
-// meanwhile form the m_j and check them.  Lanes past K add +0.0, which leaves
-// the sum unchanged (it starts at +0 and only meets non-negative values unless
-// the expert is flagged, and then its weights are flat anyway).
+// walks it 64 values at a time -- each lane converts one m_j to fp64 into LDS,
+// then every lane reads the 64 values back into registers (a broadcast) and
+// adds them in order, so each add of the chain takes VGPR operands only; the
+// next 64 are loaded while it adds.  The other waves meanwhile form the m_j
+// and check them.  Lanes past K add +0.0, which leaves the sum unchanged (it
+// starts at +0 and only meets non-negative values unless the expert is
+// flagged, and then its weights are flat anyway).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double lane_value(double v, int l) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-}
 
 __global__ void __launch_bounds__(1024) importance_kernel(const float *__restrict__ sums,
                                                           const int64_t *__restrict__ counts, int64_t K,
@@ -354,6 +350,7 @@ __global__ void __launch_bounds__(1024) importance_kernel(const float *__restric
   constexpr int NT = 1024, NW = NT / 64;
   __shared__ int s_i[NW];
   __shared__ float s_mean;
+  __shared__ __attribute__((aligned(16))) double s_chain[64];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *se = sums + static_cast<int64_t>(e) * K;
@@ -376,10 +373,21 @@ __global__ void __launch_bounds__(1024) importance_kernel(const float *__restric
     double acc = 0.0;
     float nxt = lane < K ? se[lane] : 0.0f;
     for (int64_t j0 = 0; j0 < K; j0 += 64) {
-      const double v = j0 + lane < K ? static_cast<double>(nxt / fc) : 0.0;
+      s_chain[lane] = j0 + lane < K ? static_cast<double>(nxt / fc) : 0.0;
       nxt = j0 + 64 + lane < K ? se[j0 + 64 + lane] : 0.0f;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      double v[64];
 #pragma unroll
-      for (int l = 0; l < 64; ++l) acc = acc + lane_value(v, l);
+      for (int l = 0; l < 64; l += 2) {
+        const double2 q = reinterpret_cast<const double2 *>(s_chain)[l / 2];
+        v[l] = q.x;
+        v[l + 1] = q.y;
+      }
+#pragma unroll
+      for (int l = 0; l < 64; ++l) acc = acc + v[l];
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
     if (lane == 0) s_mean = static_cast<float>(acc / static_cast<double>(K));
   }
