@@ -49,6 +49,9 @@ NORM_FLOP = {"IQ2_XXS": 24, "IQ2_XS": 24, "IQ2_S": 24, "IQ1_S": 64, "IQ1_M": 64}
 # MI355X fp32 vector peak (AMD's published dense figure): 157.3 TFLOP/s
 PEAK_TFLOPS = 157.3
 GRID_SEED = {"IQ2_XXS": 201, "IQ2_XS": 202, "IQ2_S": 203, "IQ1_S": 204, "IQ1_M": 204}
+# The pages' own encode throughput on a 5632x2048 weight (CUDA kernels on NVIDIA
+# GPUs, not this hardware; IQ2_XS not reported), for context next to ours
+PAGES_M_ELEM_S = {"IQ2_XXS": 1047.9, "IQ2_S": 725.7, "IQ1_S": 306.0, "IQ1_M": 318.0}
 
 
 def search_flop(fmt: str, rows: int, cols: int, experts: int, odd_groups: int) -> int:
@@ -314,6 +317,8 @@ def main() -> int:
         for f in api.FORMATS:
             g = torch.from_numpy(inputs.grid_for(f, GRID_SEED[f])).to(dev)
             per[f] = time_encode(f, w, g, imp, odd_groups=odd)
+            if f in PAGES_M_ELEM_S:
+                per[f]["pages_cuda_M_elem_s"] = PAGES_M_ELEM_S[f]
             log(f, per[f])
         g = torch.from_numpy(inputs.grid_for("IQ2_S", 203)).to(dev)
         ch = torch.full((rows, cols // 256, 16), 7, dtype=torch.uint8, device=dev)
