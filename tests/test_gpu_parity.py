@@ -350,6 +350,56 @@ def test_empty_inputs(api):
     assert not h.any().item()
 
 
+def test_timed_quantize_matches_and_times_the_search(api):
+    """iq_quantize_timed writes iq_quantize's payload and records its two events
+    around the search kernel (a positive duration shorter than the whole call)."""
+    say("timed quantize")
+    fmt = "IQ2_XS"
+    grid = dev(inputs.grid_for(fmt, 202))
+    w = dev_w(inputs.weight(640, 1024, 1310, 1311), "bf16")
+    imp = dev(inputs.importance_like(1024, 1312)[None, :])
+    want = host(api.quantize(fmt, w, grid, imp))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
+    got = api.quantize(fmt, w, grid, imp, events=(e0, e1))
+    w1.record()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), want)
+    assert 0.0 < e0.elapsed_time(e1) <= w0.elapsed_time(w1)
+
+
+def test_noalloc_encode_replays_in_a_graph(api):
+    """iq_quantize_noalloc captured in a HIP graph (its scratch address looked up
+    by an eager call first): every replay, with eager work in between, writes
+    the eager payload."""
+    say("noalloc graph replay")
+    fmt = "IQ2_XXS"
+    grid = dev(inputs.grid_for(fmt, 201))
+    w = dev_w(inputs.weight(256, 1024, 1320, 1321), "bf16")
+    imp = dev(inputs.importance_like(1024, 1322)[None, :])
+    want = api.quantize(fmt, w, grid, imp)
+    out = torch.empty_like(want)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        api.quantize_noalloc(fmt, w, grid, imp, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.quantize_noalloc(fmt, w, grid, imp, out=out)
+    for i in range(3):
+        out.fill_(0xA5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), i
+        other = api.quantize("IQ2_XXS", w[:64], grid, imp)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, want[:64])
+
+
 def test_encode_is_deterministic(api):
     say("determinism")
     fmt = "IQ2_S"
