@@ -1229,14 +1229,31 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   for (int k = 0; k < NCW; ++k)
 #pragma unroll
     for (int u = 0; u < U; ++u) qk[k][u] = v + U * k < NC ? s_buf[(u * NC + v + U * k) * 64 + lane] : 0.0f;
-  float4 hpre[HV4];
+  // the prefetched rows are held in one vector value: as an array of float4
+  // the compiler would place them in LDS, storing each load as it arrives and
+  // so waiting for it at once
+  typedef float hvec_t __attribute__((ext_vector_type(4 * HV4)));
+  hvec_t hpre;
+  auto h_load = [&](const float *src) {
 #pragma unroll
-  for (int t = 0; t < HV4; ++t) hpre[t] = reinterpret_cast<const float4 *>(H)[threadIdx.x + t * NT];
+    for (int t = 0; t < HV4; ++t) {
+      const float4 x = reinterpret_cast<const float4 *>(src)[threadIdx.x + t * NT];
+      hpre[4 * t] = x.x;
+      hpre[4 * t + 1] = x.y;
+      hpre[4 * t + 2] = x.z;
+      hpre[4 * t + 3] = x.w;
+    }
+  };
+  auto h_store = [&]() {
 #pragma unroll
-  for (int t = 0; t < HV4; ++t) {
-    const int f = threadIdx.x + t * NT;
-    *reinterpret_cast<float4 *>(s_h + (f >> 6) * SH + 4 * (f & 63)) = hpre[t];
-  }
+    for (int t = 0; t < HV4; ++t) {
+      const int f = threadIdx.x + t * NT;
+      *reinterpret_cast<float4 *>(s_h + (f >> 6) * SH + 4 * (f & 63)) =
+          make_float4(hpre[4 * t], hpre[4 * t + 1], hpre[4 * t + 2], hpre[4 * t + 3]);
+    }
+  };
+  h_load(H);
+  h_store();
   __syncthreads();
   // the fields of this wave's share of a revisited unit's choices do not
   // depend on the picks: they are loaded one revisit ahead, and their grid
@@ -1253,11 +1270,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
     for (int u = 0; u < U; ++u) {
       const bool more = pass == 0 || u + 1 < U;  // a next revisit exists
       const int un = (u + 1) % U;
-      if (more) {
-        const float4 *src = reinterpret_cast<const float4 *>(H + un * HROW);
-#pragma unroll
-        for (int t = 0; t < HV4; ++t) hpre[t] = src[threadIdx.x + t * NT];
-      }
+      if (more) h_load(H + un * HROW);
       // (the 32-column units score two choices per wave: their entries would
       // not fit the register budget, so they are fetched when scored)
       constexpr bool EARLY = NCW * UV <= 16;
@@ -1283,13 +1296,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
         for (int i = 0; i < UV; ++i) s_x[i][lane] = xu[i];
       }
       __syncthreads();
-      if (more) {  // every wave has formed its part: the next revisit's rows replace these
-#pragma unroll
-        for (int t = 0; t < HV4; ++t) {
-          const int f = threadIdx.x + t * NT;
-          *reinterpret_cast<float4 *>(s_h + (f >> 6) * SH + 4 * (f & 63)) = hpre[t];
-        }
-      }
+      if (more) h_store();  // every wave has formed its part: the next revisit's rows replace these
       // cross term rows i = v, v + U, ...: the parts added in unit order
 #pragma unroll
       for (int t = 0; t < NI; ++t) {
