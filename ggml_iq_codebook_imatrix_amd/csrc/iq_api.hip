@@ -72,7 +72,9 @@ int check_encode_shape(int64_t rows, int64_t cols, int64_t rpe, int fmt, int64_t
   return IQ_OK;
 }
 
-int64_t wg_cols(int fmt) { return 32 / (fmt == IQ_FMT_IQ1_M ? 8 : 4); }
+// search workgroups per block column: 32 groups over the groups per workgroup
+// (eight for IQ2_XXS, IQ2_XS and IQ1_M, four for IQ2_S and IQ1_S)
+int64_t wg_cols(int fmt) { return (fmt == IQ_FMT_IQ2_S || fmt == IQ_FMT_IQ1_S) ? 8 : 4; }
 
 int check_workspace(size_t need, const void *ws, size_t ws_bytes) {
   if (need == 0) return IQ_OK;

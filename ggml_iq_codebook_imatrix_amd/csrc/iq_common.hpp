@@ -19,27 +19,29 @@ namespace iq {
 enum Fmt : int { IQ2_XXS = 0, IQ2_XS = 1, IQ2_S = 2, IQ1_S = 3, IQ1_M = 4 };
 
 // Per-format geometry.  GPU = 8-value groups per choice unit; NC = choices per
-// unit; WGG = groups (one wave each) per search workgroup -- the smallest set of
-// groups whose payload bytes no other workgroup touches.
+// unit; PG = groups per packed unit, the smallest set of groups whose payload
+// bytes no other set touches; WGG = groups (one wave each) per search
+// workgroup, a multiple of PG (eight for the layouts whose groups are sorted
+// by parity, so the sort deals from more items).
 template <int F> struct Geo;
 template <> struct Geo<IQ2_XXS> {
-  static constexpr int BYTES = 66, N = 256, GPU = 4, UNITS = 8, NC = 16, WGG = 4;
+  static constexpr int BYTES = 66, N = 256, GPU = 4, UNITS = 8, NC = 16, PG = 4, WGG = 8;
   static constexpr bool IQ1 = false, PARITY = true;
 };
 template <> struct Geo<IQ2_XS> {
-  static constexpr int BYTES = 74, N = 512, GPU = 2, UNITS = 16, NC = 16, WGG = 4;
+  static constexpr int BYTES = 74, N = 512, GPU = 2, UNITS = 16, NC = 16, PG = 4, WGG = 8;
   static constexpr bool IQ1 = false, PARITY = true;
 };
 template <> struct Geo<IQ2_S> {
-  static constexpr int BYTES = 82, N = 1024, GPU = 2, UNITS = 16, NC = 16, WGG = 4;
+  static constexpr int BYTES = 82, N = 1024, GPU = 2, UNITS = 16, NC = 16, PG = 4, WGG = 4;
   static constexpr bool IQ1 = false, PARITY = false;
 };
 template <> struct Geo<IQ1_S> {
-  static constexpr int BYTES = 50, N = 2048, GPU = 4, UNITS = 8, NC = 16, WGG = 4;
+  static constexpr int BYTES = 50, N = 2048, GPU = 4, UNITS = 8, NC = 16, PG = 4, WGG = 4;
   static constexpr bool IQ1 = true, PARITY = false;
 };
 template <> struct Geo<IQ1_M> {
-  static constexpr int BYTES = 56, N = 2048, GPU = 2, UNITS = 16, NC = 8, WGG = 8;
+  static constexpr int BYTES = 56, N = 2048, GPU = 2, UNITS = 16, NC = 8, PG = 8, WGG = 8;
   static constexpr bool IQ1 = true, PARITY = false;
 };
 

@@ -385,10 +385,10 @@ __device__ __forceinline__ uint32_t pack_record(const GroupFields &f) {
 }
 
 // ---------------------------------------------------------------------------
-// Pack one workgroup's bytes of one row's block from the LDS field tables:
-// k[g][row], m[g][row] (IQ2 sign mask / IQ1 shift), c[u][row] (unit choice).
-// Workgroup sb owns: IQ2_XXS/XS/S, IQ1_S the 32-value sub-block sb; IQ1_M the
-// 64 values of scale word sb.
+// Pack one packed unit's bytes of one row's block from the LDS field tables:
+// k[g][row], m[g][row] (IQ2 sign mask / IQ1 shift), c[u][row] (unit choice),
+// the unit's PG groups first.  Packed unit sb is: IQ2_XXS/XS/S, IQ1_S the
+// 32-value sub-block sb; IQ1_M the 64 values of scale word sb.
 // ---------------------------------------------------------------------------
 template <int F>
 __device__ __forceinline__ void pack_bytes(uint8_t *blk, int sb, int lane, const uint16_t (*s_k)[64],
@@ -502,9 +502,9 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   __shared__ uint8_t s_m[WGG][64];
   __shared__ uint8_t s_c[UPW][64];
   // Parity-sorted items (IQ2_XXS/XS, every mode): the workgroup's WGG x 64
-  // (group, row) items are dealt to the waves odd-parity first, so about one
-  // wave in three holds only even-parity groups and sweeps without the parity
-  // term.  A wave then mixes groups, so the weighted norms come from an LDS
+  // (group, row) items are dealt to the waves odd-parity first, so of the
+  // eight waves about three hold only even-parity groups and sweep without the
+  // parity term (and at most one mixes both).  A wave then mixes groups, so the weighted norms come from an LDS
   // copy of the workgroup's tables instead of scalar loads (the every-choice
   // rescans read the same copy), and the LDS field tables are indexed by each
   // item's group and row.
@@ -729,11 +729,12 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
       s_m[gw][rl] = static_cast<uint8_t>(mfield);
       if (gw % GPU == 0) s_c[uw][rl] = static_cast<uint8_t>(cu);
       __syncthreads();
-      // wave 0 packs the tile's rows, lane = row
-      if (wave == 0 && tile * 64 + lane < A.rpe) {
+      // wave p packs packed unit p of the workgroup for the tile's rows, lane = row
+      constexpr int PPW = WGG / G::PG;
+      if (wave < PPW && tile * 64 + lane < A.rpe) {
         const int64_t rp = e * A.rpe + tile * 64 + lane;
-        pack_bytes<F>(A.out + c * A.copy_stride + (rp * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c,
-                      A.dscr[rp * A.nb + b]);
+        pack_bytes<F>(A.out + c * A.copy_stride + (rp * A.nb + b) * G::BYTES, sb * PPW + wave, lane,
+                      s_k + wave * G::PG, s_m + wave * G::PG, s_c + wave * (G::PG / GPU), A.dscr[rp * A.nb + b]);
       }
     }
     return;
@@ -816,11 +817,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   s_m[gw][rl] = static_cast<uint8_t>(mfield);
   if (gw % GPU == 0) s_c[uw][rl] = static_cast<uint8_t>(cu);
   __syncthreads();
-  // wave 0 packs the tile's rows, lane = row (the row and its scale are
-  // recomputed here rather than kept through the sweep)
-  if (wave != 0 || tile * 64 + lane >= A.rpe) return;
+  // wave p packs packed unit p of the workgroup's PPW, lane = row (the row and
+  // its scale are recomputed here rather than kept through the sweep)
+  constexpr int PPW = WGG / G::PG;
+  if (wave >= PPW || tile * 64 + lane >= A.rpe) return;
   const int64_t rp = e * A.rpe + tile * 64 + lane;
-  pack_bytes<F>(A.out + (rp * A.nb + b) * G::BYTES, sb, lane, s_k, s_m, s_c, A.dscr[rp * A.nb + b]);
+  pack_bytes<F>(A.out + (rp * A.nb + b) * G::BYTES, sb * PPW + wave, lane, s_k + wave * G::PG, s_m + wave * G::PG,
+                s_c + wave * (G::PG / GPU), A.dscr[rp * A.nb + b]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1367,8 +1370,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
 
   // payload under the picks: each wave stages its unit's fields (the parts
   // buffer is free: its last reader is two barriers back), then wave sb packs
-  // sub-block sb as the search kernel does
-  constexpr int WGG = G::WGG, SBS = 32 / WGG, UPW = WGG / GPU;
+  // packed unit sb as the search kernel does
+  constexpr int PG = G::PG, SBS = 32 / PG, UPW = PG / GPU;
   uint16_t(*p_k)[64] = reinterpret_cast<uint16_t(*)[64]>(s_buf);
   uint8_t(*p_m)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2);
   uint8_t(*p_c)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2 + 32 * 64 / 4);
@@ -1383,7 +1386,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   __syncthreads();
   if (v < SBS && valid) {
     uint8_t *blk = A.out + (r * A.nb + b) * G::BYTES;
-    pack_bytes<F>(blk, v, lane, p_k + v * WGG, p_m + v * WGG, p_c + v * UPW, d16);
+    pack_bytes<F>(blk, v, lane, p_k + v * PG, p_m + v * PG, p_c + v * UPW, d16);
     if (F != IQ1_M && v == 0) *reinterpret_cast<uint16_t *>(blk) = d16;
   }
 }
