@@ -333,14 +333,25 @@ int launch_collect(const void *x, int dtype, int64_t T, int64_t K, const int32_t
 // Importance.  a_j = sqrt(max(m_j, floor_rel * mean)), m_j = sums_j / count
 // (IEEE fp32 division and square root).  The mean is the plain one: the m_j
 // added one after another in fp64, j ascending from 0, the total divided by K
-// in fp64 and rounded to fp32.  That running sum is one dependent chain: wave 0
-// walks it 64 values at a time -- each lane converts one m_j to fp64 into LDS,
-// then every lane reads the 64 values back into registers (a broadcast) and
-// adds them in order, so each add of the chain takes VGPR operands only; the
-// next 64 are loaded while it adds.  The other waves meanwhile form the m_j
-// and check them.  Lanes past K add +0.0, which leaves the sum unchanged (it
-// starts at +0 and only meets non-negative values unless the expert is
-// flagged, and then its weights are flat anyway).
+// in fp64 and rounded to fp32.
+//
+// When no partial sum can round, every order of additions gives that running
+// sum, so the workgroup adds the m_j in parallel.  The non-negative fp32 m_j
+// are all integer multiples of q, the least ulp among the nonzero ones, and so
+// is every partial sum in any order; a partial sum below 2^53 q is then exact
+// in fp64.  All of them lie below the true total S, so S < 2^53 q suffices.
+// The parallel fp64 total S' of n non-negative terms satisfies
+// S <= S' (1 + (n + 4) 2^-52) (each of at most n - 1 additions rounds by a
+// relative 2^-53), so S' (1 + (n + 4) 2^-52) < 2^53 q proves it, and S' is
+// then exactly the running sum.
+//
+// Otherwise the running sum is one dependent chain: wave 0 walks it 64 values
+// at a time -- each lane converts one m_j to fp64 into LDS, then every lane
+// reads the 64 values back into registers (a broadcast) and adds them in
+// order, so each add of the chain takes VGPR operands only; the next 64 are
+// loaded while it adds.  Lanes past K add +0.0, which leaves the sum unchanged
+// (it starts at +0 and only meets non-negative values).  A flagged expert
+// (a value negative or not finite) takes flat weights without a mean.
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(1024) importance_kernel(const float *__restrict__ sums,
@@ -348,7 +359,8 @@ __global__ void __launch_bounds__(1024) importance_kernel(const float *__restric
                                                           float floor_rel, float *__restrict__ imp,
                                                           int32_t *status) {
   constexpr int NT = 1024, NW = NT / 64;
-  __shared__ int s_i[NW];
+  __shared__ int s_i[NW], s_u[NW];
+  __shared__ double s_s[NW];
   __shared__ float s_mean;
   __shared__ __attribute__((aligned(16))) double s_chain[64];
   const int e = blockIdx.x;
@@ -362,40 +374,68 @@ __global__ void __launch_bounds__(1024) importance_kernel(const float *__restric
   }
   const float fc = static_cast<float>(c);
   int bad = 0;
+  int umin = 1 << 20;  // least ulp exponent among the nonzero m_j
+  double part = 0.0;
   for (int64_t j = tid; j < K; j += NT) {
     const float m = se[j] / fc;
     bad |= !(finite_f(m) && m >= 0.0f);
+    if (m > 0.0f) {
+      const int ef = static_cast<int>(__float_as_uint(m) >> 23);  // biased exponent (sign is 0)
+      umin = min(umin, (ef > 1 ? ef : 1) - 150);
+    }
+    part += static_cast<double>(m);
     ie[j] = m;  // m_j kept in the output until the floor is known
   }
-  for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
-  if (lane == 0) s_i[wave] = bad;
-  if (wave == 0) {
-    double acc = 0.0;
-    float nxt = lane < K ? se[lane] : 0.0f;
-    for (int64_t j0 = 0; j0 < K; j0 += 64) {
-      s_chain[lane] = j0 + lane < K ? static_cast<double>(nxt / fc) : 0.0;
-      nxt = j0 + 64 + lane < K ? se[j0 + 64 + lane] : 0.0f;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      double v[64];
-#pragma unroll
-      for (int l = 0; l < 64; l += 2) {
-        const double2 q = reinterpret_cast<const double2 *>(s_chain)[l / 2];
-        v[l] = q.x;
-        v[l + 1] = q.y;
-      }
-#pragma unroll
-      for (int l = 0; l < 64; ++l) acc = acc + v[l];
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-    if (lane == 0) s_mean = static_cast<float>(acc / static_cast<double>(K));
+  for (int o = 32; o > 0; o >>= 1) {
+    bad |= __shfl_xor(bad, o);
+    umin = min(umin, __shfl_xor(umin, o));
+    part += __shfl_xor(part, o);
+  }
+  if (lane == 0) {
+    s_i[wave] = bad;
+    s_u[wave] = umin;
+    s_s[wave] = part;
   }
   __syncthreads();
   bad = 0;
-  for (int w = 0; w < NW; ++w) bad |= s_i[w];
-  const float mean = s_mean;
+  umin = 1 << 20;
+  double tot = 0.0;
+  for (int w = 0; w < NW; ++w) {
+    bad |= s_i[w];
+    umin = min(umin, s_u[w]);
+    tot += s_s[w];
+  }
+  // exact in any order when tot (1 + (K + 4) 2^-52) < 2^53 q (all-zero: tot = 0)
+  const bool exact = umin > (1 << 19) || tot * (1.0 + static_cast<double>(K + 4) * 0x1p-52) < ldexp(1.0, umin + 53);
+  if (wave == 0 && !bad) {
+    if (exact) {
+      if (lane == 0) s_mean = static_cast<float>(tot / static_cast<double>(K));
+    } else {
+      double acc = 0.0;
+      float nxt = lane < K ? se[lane] : 0.0f;
+      for (int64_t j0 = 0; j0 < K; j0 += 64) {
+        s_chain[lane] = j0 + lane < K ? static_cast<double>(nxt / fc) : 0.0;
+        nxt = j0 + 64 + lane < K ? se[j0 + 64 + lane] : 0.0f;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        double v[64];
+#pragma unroll
+        for (int l = 0; l < 64; l += 2) {
+          const double2 q = reinterpret_cast<const double2 *>(s_chain)[l / 2];
+          v[l] = q.x;
+          v[l + 1] = q.y;
+        }
+#pragma unroll
+        for (int l = 0; l < 64; ++l) acc = acc + v[l];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+      if (lane == 0) s_mean = static_cast<float>(acc / static_cast<double>(K));
+    }
+  }
+  __syncthreads();
   if (bad && tid == 0) raise_status(status, ST_BADIMP);
+  const float mean = bad ? 0.0f : s_mean;
   if (bad || mean == 0.0f) {  // nothing usable: flat weights
     for (int64_t j = tid; j < K; j += NT) ie[j] = 1.0f;
     return;

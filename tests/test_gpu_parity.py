@@ -570,20 +570,23 @@ def test_importance_parity(api, orc):
 def test_importance_mean_is_the_sequential_fp64_mean(api, orc):
     """The floor's mean on the device is the running fp64 sum in ascending j:
     floor_rel = 1 makes every value below the mean take sqrt(mean) exactly, so
-    the mean's fp32 bits show.  Wide-range statistics (lognormal(0, 6)) at
-    several widths, plus a hand case whose sequential mean is an fp32 midpoint
-    (0.5 + 2^-25, rounding to 0.5) while the exact or pairwise mean rounds up."""
+    the mean's fp32 bits show.  Narrow-range statistics (lognormal(0, 0.5):
+    no partial sum can round, the device adds in parallel) and wide-range ones
+    (lognormal(0, 6): the device walks the chain) at several widths, plus a hand
+    case whose sequential mean is an fp32 midpoint (0.5 + 2^-25, rounding to
+    0.5) while the exact or pairwise mean rounds up."""
     say("importance sequential mean")
     g = inputs.rng(1710)
-    for K in (1, 63, 64, 65, 2048, 5000, 17408):
-        E = 3
-        sums = g.lognormal(0, 6, (E, K)).astype(np.float32)
-        sums[:, g.random(K) < 0.1] = 0.0
-        counts = np.array([1, 3, 977], np.int64)
-        for fl in (1e-6, 1.0):
-            got = host(api.imatrix_importance(dev(sums), dev(counts), fl))
-            want, _ = orc.importance(sums, counts, fl)
-            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (K, fl)
+    for sigma in (0.5, 6.0):
+        for K in (1, 63, 64, 65, 2048, 5000, 17408):
+            E = 3
+            sums = g.lognormal(0, sigma, (E, K)).astype(np.float32)
+            sums[:, g.random(K) < 0.1] = 0.0
+            counts = np.array([1, 3, 977], np.int64)
+            for fl in (1e-6, 1.0):
+                got = host(api.imatrix_importance(dev(sums), dev(counts), fl))
+                want, _ = orc.importance(sums, counts, fl)
+                assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (sigma, K, fl)
     hand = np.array([[4.0, 2.0 ** -22] + [2.0 ** -52] * 6], np.float32)
     got = host(api.imatrix_importance(dev(hand), dev(np.array([1], np.int64)), 1.0))
     assert got[0, 2] == np.sqrt(np.float32(0.5))
