@@ -1,4 +1,4 @@
-/* Driver for running the CPU oracle under AddressSanitizer and
+/* Test program that runs the CPU oracle under AddressSanitizer and
  * UndefinedBehaviorSanitizer: calls every exported oracle function on small
  * seeded inputs, including the edge cases the oracle flags (zero, non-finite
  * and overflowing blocks, out-of-range ids and choices, importance above
