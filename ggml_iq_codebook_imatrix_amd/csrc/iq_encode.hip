@@ -303,30 +303,36 @@ __device__ __forceinline__ float to_vgpr(float s) {
 // ---------------------------------------------------------------------------
 // Rescan one CH-entry chunk under one (scale, shift) slot: the first entry with
 // the least reduced error -- the same fp32 values the sweep compared -- and
-// its sign mask (IQ2) or shift bit (IQ1).
+// its sign mask (IQ2) or shift bit (IQ1).  par = false (a wave whose groups
+// all have even parity) drops the parity term as that wave's sweep did.
 // ---------------------------------------------------------------------------
 template <int F, int CH>
 __device__ __forceinline__ void rescan_chunk(const float *__restrict__ grid, const float *gt, const GroupState<F> &S,
-                                             int chs, float ssel, int hsel, int &kb, uint32_t &mfield) {
+                                             int chs, float ssel, int hsel, bool par, int &kb, uint32_t &mfield) {
   using G = Geo<F>;
   constexpr int N = G::N;
   const float dsel = hsel ? -0.125f : 0.125f;
   float bt = __builtin_inff();
   kb = chs * CH;
-  for (int i = 0; i < CH; ++i) {
-    const int k = chs * CH + i;
-    float g[8];
-    load_entry(grid + static_cast<int64_t>(k) * 8, g);
-    const float q2 = S.term(g);
-    float t;
-    if (!G::IQ1) {
-      t = __builtin_fmaf(ssel, gt[k], q2);
-    } else {
-      const float pn = __builtin_fmaf(dsel, S.S2, q2);
-      t = __builtin_fmaf(ssel, gt[hsel * N + k], pn);
+  auto scan = [&](auto pc) {
+    constexpr bool PAR = decltype(pc)::value;
+    for (int i = 0; i < CH; ++i) {
+      const int k = chs * CH + i;
+      float g[8];
+      load_entry(grid + static_cast<int64_t>(k) * 8, g);
+      const float q2 = S.template term<PAR>(g);
+      float t;
+      if (!G::IQ1) {
+        t = __builtin_fmaf(ssel, gt[k], q2);
+      } else {
+        const float pn = __builtin_fmaf(dsel, S.S2, q2);
+        t = __builtin_fmaf(ssel, gt[hsel * N + k], pn);
+      }
+      if (t < bt) { bt = t; kb = k; }
     }
-    if (t < bt) { bt = t; kb = k; }
-  }
+  };
+  if (G::PARITY && par) scan(std::integral_constant<bool, G::PARITY>{});
+  else scan(std::integral_constant<bool, false>{});
   if (!G::IQ1) {
     uint32_t mask = S.neg;
     if (S.odd) {
@@ -349,21 +355,26 @@ __device__ __forceinline__ int lds_entry(int k) { return k * 8 + (k / CH) * 4; }
 
 template <int F, int CH, bool TAB>
 __device__ __forceinline__ void rescan_chunk_lds(const float *s_grid, const float *gnorm, const float a[8],
-                                                 const GroupState<F> &S, int chs, float ssel, int &kb,
+                                                 const GroupState<F> &S, int chs, float ssel, bool par, int &kb,
                                                  uint32_t &mfield) {
   float bt = __builtin_inff();
   kb = chs * CH;
   const float *base = s_grid + lds_entry<CH>(chs * CH);
+  auto scan = [&](auto pc) {
+    constexpr bool PAR = decltype(pc)::value;
 #pragma unroll 4
-  for (int i = 0; i < CH; ++i) {
-    float g[8];
-    load_entry(base + i * 8, g);
-    // the weighted norm: the workgroup's LDS table (TAB), else the same fmaf
-    // chain in the lane
-    const float gk = TAB ? gnorm[chs * CH + i] : iq2_norm(a, g);
-    const float t = __builtin_fmaf(ssel, gk, S.term(g));
-    if (t < bt) { bt = t; kb = chs * CH + i; }
-  }
+    for (int i = 0; i < CH; ++i) {
+      float g[8];
+      load_entry(base + i * 8, g);
+      // the weighted norm: the workgroup's LDS table (TAB), else the same fmaf
+      // chain in the lane
+      const float gk = TAB ? gnorm[chs * CH + i] : iq2_norm(a, g);
+      const float t = __builtin_fmaf(ssel, gk, S.template term<PAR>(g));
+      if (t < bt) { bt = t; kb = chs * CH + i; }
+    }
+  };
+  if (Geo<F>::PARITY && par) scan(std::integral_constant<bool, Geo<F>::PARITY>{});
+  else scan(std::integral_constant<bool, false>{});
   uint32_t mask = S.neg;
   if (S.odd) {
     float g[8];
@@ -695,8 +706,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (LDS_RESCAN) rescan_chunk_lds<F, CH, SORTED>(s_u, SORTED ? &s_g[gw][0] : s_u, a, S, chs, ssel, kb, mfield);
-      else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F, CH, SORTED>(s_u, SORTED ? &s_g[gw][0] : s_u, a, S, chs, ssel, !all_even, kb, mfield);
+      else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, !all_even, kb, mfield);
       GroupFields f;
       f.d16 = d16;
       f.k = static_cast<uint32_t>(kb);
@@ -720,8 +731,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
       const float ssel = G::IQ1 ? sc[c & 7] : sc[c];
       int kb;
       uint32_t mfield;
-      if (LDS_RESCAN) rescan_chunk_lds<F, CH, SORTED>(s_u, SORTED ? &s_g[gw][0] : s_u, a, S, chs, ssel, kb, mfield);
-      else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, kb, mfield);
+      if (LDS_RESCAN) rescan_chunk_lds<F, CH, SORTED>(s_u, SORTED ? &s_g[gw][0] : s_u, a, S, chs, ssel, !all_even, kb, mfield);
+      else rescan_chunk<F, CH>(A.grid, gt, S, chs, ssel, G::IQ1 ? (slot >> 3) : 0, !all_even, kb, mfield);
       int cu = c;
       if (d16 == 0) { kb = 0; mfield = 0; cu = 0; }
       __syncthreads();  // the previous choice's bytes have been read from LDS
@@ -809,7 +820,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   }
   int kb;
   uint32_t mfield;
-  rescan_chunk<F, CH>(A.grid, SORTED ? &s_g[gw][0] : gt, S, chs, ssel, hsel, kb, mfield);
+  rescan_chunk<F, CH>(A.grid, SORTED ? &s_g[gw][0] : gt, S, chs, ssel, hsel, !all_even, kb, mfield);
   if (zero_blk) { kb = 0; mfield = 0; cu = 0; }
 
   // ---- pack ----------------------------------------------------------------
