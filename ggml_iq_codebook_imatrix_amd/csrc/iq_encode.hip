@@ -944,16 +944,26 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
 // ---------------------------------------------------------------------------
 // Local-Hessian choice search (ModelOpt PR #3158).  Damping of the diagonal
 // Hessian blocks: lambda = perc_damp * mean(diag H_b), the diagonal summed in
-// fp64 and the mean rounded to fp32.
+// fp64 (j ascending) and the mean rounded to fp32.  One wave per block: the
+// lanes fetch the 256 diagonal entries (each in its own cache line) together,
+// then lane 0 walks the running sum from LDS.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) damping_kernel(const float *__restrict__ hess, int64_t n, float perc_damp,
-                                                       float *__restrict__ lam) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+__global__ void __launch_bounds__(64) damping_kernel(const float *__restrict__ hess, float perc_damp,
+                                                      float *__restrict__ lam) {
+  __shared__ double s_d[256];
+  const int64_t i = blockIdx.x;
   const float *H = hess + i * 65536;
-  double acc = 0.0;
-  for (int j = 0; j < 256; ++j) acc += static_cast<double>(H[j * 257]);
-  lam[i] = perc_damp * static_cast<float>(acc / 256.0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = static_cast<int>(threadIdx.x) + 64 * t;
+    s_d[j] = static_cast<double>(H[j * 257]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int j = 0; j < 256; ++j) acc += s_d[j];
+    lam[i] = perc_damp * static_cast<float>(acc / 256.0);
+  }
 }
 
 // the unit's weights (the same under every choice)
@@ -1532,8 +1542,7 @@ static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp,
   E.copies = 0;
   E.rec = rec;
   if (launch_quantize_t<F>(E, RECORDS, qws, nullptr, nullptr, stream) != 0) return -1;
-  hipLaunchKernelGGL(damping_kernel, dim3(static_cast<unsigned>((nl + 255) / 256)), dim3(256), 0, stream, hess, nl,
-                     perc_damp, lam);
+  hipLaunchKernelGGL(damping_kernel, dim3(static_cast<unsigned>(nl)), dim3(64), 0, stream, hess, perc_damp, lam);
   if (!launched_ok()) return -1;
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb;
