@@ -320,6 +320,40 @@ def test_choice_search_full_size_sampled(api, orc, fmt):
     assert np.array_equal(pay[rid], pw)
 
 
+def test_choice_search_moe_sampled(api, orc):
+    """The fused-MoE local-Hessian path at its bench size: 128 experts of
+    768x2048 bf16, per-expert Hessian blocks from the routed tokens (the
+    device's, fed to both sides) and importance, one choice-search launch with
+    the payload; sampled rows, every idle expert's included, against the oracle."""
+    say("choice search moe")
+    w, x, ids, grid, spec = inputs.moe_workload()
+    E, rpe = spec["experts"], spec["rows_per_expert"]
+    xd, idsd = dev_w(x, "bf16"), dev(ids)
+    sums, counts = api.imatrix_collect(xd, idsd, E, chunk_rows=1024)
+    imp = api.imatrix_importance(sums, counts)
+    hess = api.hessian_collect(xd, idsd, E)
+    got, pay = api.choice_search("IQ2_XXS", dev_w(w, "bf16"), dev(grid), hess, imp, rows_per_expert=rpe,
+                                 payload=True)
+    got, pay, hess_h, imp_h, c = host(got), host(pay), host(hess), host(imp), host(counts)
+    idle = np.flatnonzero(c == 0)
+    assert idle.size >= 5
+    extra = np.concatenate([[e * rpe, e * rpe + rpe - 1] for e in idle])
+    rid = sample_rows(w.shape[0], 2500, extra)
+    full = got.copy()
+    for k0 in range(0, rid.size, 8192):  # (every row with IQ_FULL_PARITY=1: a line per 8,192)
+        part = rid[k0:k0 + 8192]
+        want, _ = orc.choice_search("IQ2_XXS", w, grid, hess_h, imp_h, rows_per_expert=rpe, row_ids=part,
+                                    threads=THREADS)
+        bad = np.argwhere(got[part] != want)
+        assert bad.size == 0, f"{len(bad)} picks differ, first {bad[:5].tolist()}"
+        full[part] = want
+        pw, _ = orc.quantize("IQ2_XXS", w, grid, imp_h, rows_per_expert=rpe, choices=full, row_ids=part,
+                             threads=THREADS)
+        bad = np.argwhere((pay[part] != pw).any(axis=-1))
+        assert bad.size == 0, f"{len(bad)} blocks differ, first {bad[:5].tolist()}"
+        say("choice search moe rows", k0 + part.size, "of", rid.size)
+
+
 def test_empty_inputs(api):
     """Zero rows or tokens: every entry point returns without launching and
     leaves the outputs as they were."""
