@@ -137,6 +137,28 @@ def measured_valu_peak(iters: int = 2000) -> dict:
     return out
 
 
+def settle_clocks(seconds: float) -> dict:
+    """Hold every CU under the ceiling's VGPR-only FMA stream for `seconds`
+    before anything is measured; returns how long, how many runs, and the
+    shader clock of the last one.  A fresh or idle MI355X meets a burst of work
+    ~13% below its sustained clock and needs ~10-20 ms of full load to reach it
+    (the microbenchmark back to back: 1.79 GHz in its first runs, 2.04-2.07 GHz
+    from ~20 ms on), so a warm-up of a few steps would otherwise time the ramp
+    rather than the kernels."""
+    import ctypes
+    L = _peak_lib()
+    d = ctypes.c_double
+    clk = d()
+    t0 = time.perf_counter()
+    runs = 0
+    while runs == 0 or time.perf_counter() - t0 < seconds:
+        ops, ins = d(), d()
+        if L.valu_peak(0, 8000, ctypes.byref(ops), ctypes.byref(ins), ctypes.byref(clk)) != 0:
+            raise RuntimeError("valu_peak failed")
+        runs += 1
+    return {"seconds": round(time.perf_counter() - t0, 3), "runs": runs, "clock_GHz": round(clk.value / 1e9, 3)}
+
+
 def best_ceiling(a: dict, b: dict) -> dict:
     """Of two ceiling measurements, the one with the higher FMA rate (the
     clocks ramp on a fresh box, so a run can catch them low)."""
@@ -171,6 +193,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--settle-s", type=float, default=0.25,
+                    help="seconds of full-chip VALU load before the ceiling and the steps (0: none)")
     ap.add_argument("--reps", type=int, default=10, help="repetitions per extra encode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the per-layout / MoE / 17408x5120 tables")
@@ -239,9 +263,11 @@ def main() -> int:
                      events=None if i is None or i % EVENT_STRIDE else (ev_s[i], ev_e[i]))
         api.dequantize(fmt, packed, grid, out=w_hat)
 
-    # the measured ceilings run first: they also bring the clocks up before the
-    # untimed warm-up steps; they run again after the timed steps and the
-    # higher of the two is the ceiling
+    # the clocks are brought up first, then the measured ceilings run (again
+    # after the timed steps; the higher of the two is the ceiling), then the
+    # untimed warm-up steps
+    settle = settle_clocks(args.settle_s) if args.settle_s > 0 else None
+    log("clocks settled", settle)
     meas0 = measured_valu_peak()
     log("measured VALU ceiling (before)", meas0)
     for _ in range(args.warmup):
@@ -281,7 +307,8 @@ def main() -> int:
                 "ms_per_launch": round(search_ms, 4), "launches_timed": len(timed_steps),
                 "measured_fma_TFLOP_s": meas["fma_TFLOP_s"],
                 "frac_of_measured_fma": frac_measured(achieved, meas["fma_TFLOP_s"]),
-                "clock_GHz_ceiling_run": meas["clock_GHz"], "clock_GHz_after_timed_steps": clock_after}
+                "clock_GHz_ceiling_run": meas["clock_GHz"], "clock_GHz_after_timed_steps": clock_after,
+                "clock_settle": settle}
     roofline["measured"] = meas
 
     # ---------------- extras: every layout on the same weight --------------
