@@ -312,6 +312,13 @@ def main() -> int:
     roofline["measured"] = meas
 
     # ---------------- extras: every layout on the same weight --------------
+    # each measurement below follows host-side set-up that leaves the chip
+    # idle, so the clocks are brought up again before it (0.05 s: the ramp
+    # takes ~10-20 ms), else a burst of a few ms would time the ramp
+    def resettle():
+        if args.settle_s > 0:
+            settle_clocks(min(args.settle_s, 0.05))
+
     extras = {}
     if not args.no_extras:
         def time_encode(f, wd, g, impd, rpe=None, choices=None, reps=args.reps, odd_groups=None):
@@ -319,6 +326,7 @@ def main() -> int:
                              dtype=torch.uint8, device=dev)
             out = api.quantize(f, wd, g, impd, rows_per_expert=rpe, choices=choices, workspace=ws)
             torch.cuda.synchronize()
+            resettle()
             es = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
             ee = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
             ks = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
@@ -363,6 +371,7 @@ def main() -> int:
             g = torch.from_numpy(inputs.grid_for(f, GRID_SEED[f])).to(dev)
             out = api.quantize_every_choice(f, w, g, imp)
             torch.cuda.synchronize()
+            resettle()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(args.reps):
@@ -384,6 +393,7 @@ def main() -> int:
         def timed(fn, reps):
             fn()
             torch.cuda.synchronize()
+            resettle()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(reps):
@@ -436,6 +446,7 @@ def main() -> int:
         del wm, xm
         s3, c3 = api.imatrix_collect(xmd, idsd, E, chunk_rows=1024)
         torch.cuda.synchronize()
+        resettle()
         ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ce0.record()
         for _ in range(args.reps):
