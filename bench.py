@@ -12,7 +12,8 @@ Also reported: the dominant kernel's roofline (the encoder's search kernel,
 timed alone with HIP events around its own launches in every EVENT_STRIDE-th
 timed step: an event pair costs the stream some 15-20 us, ~2.5% of a step, so
 not every step carries one) in FLOP against the fp32
-vector peak and against the fp32 FMA rate measured on the same chip, per-layout
+vector peak and against the VALU instruction rate measured on the same chip
+(twice the fastest of three instruction streams, in FLOP), per-layout
 encode throughput on the same weight, the fixed-choice IQ2_S variant, the IQ1
 layouts on 17408x5120, the fused-MoE workload, and the CPU oracle's throughput
 on a bounded sample of the same step.
@@ -114,11 +115,15 @@ def measured_valu_peak(iters: int = 2000) -> dict:
     """What this GPU sustains for the sweep's instruction forms (independent
     chains, 8 waves per SIMD, built like the encoder): VGPR-only fp32 FMA, the
     3-input min, and the candidate mix of two FMAs per 3-input min; in
-    algorithmic ops (FMA 1, 3-input min 2), with the shader clock measured
-    during the run.  In FLOP the VGPR-only FMA stream is the fastest form the
-    search issues (2 FLOP per instruction, co-issued across waves; a 3-input
-    min is also 2 FLOP but does not co-issue, and no packed fp32 is used), so
-    2 x its rate bounds the search's FLOP rate on this chip at this clock.
+    algorithmic ops (FMA 1, 3-input min 2) and in instructions, with the shader
+    clock measured during the run.  By the work model every instruction the
+    search issues carries at most 2 FLOP (an FMA or a 3-input min), so its FLOP
+    rate is at most twice its instruction rate; the ceiling is twice the highest
+    instruction rate of the three streams.  That is the mix: an FMA pairs with a
+    3-input min as well as with another FMA, so it retires more instructions
+    than the FMA stream (about 1.7x against 1.6x one wave instruction per SIMD
+    per 4 clocks; the 3-input min alone stays at 1.0x).  It is a measured
+    reference, not a proof: a stream with a better pairing would pass it.
     From libvalu_peak.so (ggml_iq_codebook_imatrix_amd/peak)."""
     import ctypes
     L = _peak_lib()
@@ -133,6 +138,7 @@ def measured_valu_peak(iters: int = 2000) -> dict:
         out[f"{name}_Tinstr_s"] = round(ins.value / 1e12, 2)
         clocks.append(clk.value)
     out["fma_TFLOP_s"] = round(out["fma_TOP_s"] * 2, 2)
+    out["ceiling_TFLOP_s"] = round(2 * max(out["fma_Tinstr_s"], out["min3_Tinstr_s"], out["mix_Tinstr_s"]), 2)
     out["clock_GHz"] = round(min(clocks) / 1e9, 3) if min(clocks) > 0 else None
     return out
 
@@ -160,9 +166,9 @@ def settle_clocks(seconds: float) -> dict:
 
 
 def best_ceiling(a: dict, b: dict) -> dict:
-    """Of two ceiling measurements, the one with the higher FMA rate (the
-    clocks ramp on a fresh box, so a run can catch them low)."""
-    return a if a["fma_TFLOP_s"] >= b["fma_TFLOP_s"] else b
+    """Of two ceiling measurements, the higher one (a run can catch the clocks
+    lower than the other)."""
+    return a if a["ceiling_TFLOP_s"] >= b["ceiling_TFLOP_s"] else b
 
 
 def shader_clock_ghz(us: int = 200) -> float | None:
@@ -305,8 +311,8 @@ def main() -> int:
                 "kernel": "search_kernel<IQ2_XS>", "flop_per_launch": flop,
                 "flop_per_elem": round(flop / (rows * cols), 1), "odd_parity_groups": odd,
                 "ms_per_launch": round(search_ms, 4), "launches_timed": len(timed_steps),
-                "measured_fma_TFLOP_s": meas["fma_TFLOP_s"],
-                "frac_of_measured_fma": frac_measured(achieved, meas["fma_TFLOP_s"]),
+                "measured_ceiling_TFLOP_s": meas["ceiling_TFLOP_s"],
+                "frac_of_measured_ceiling": frac_measured(achieved, meas["ceiling_TFLOP_s"]),
                 "clock_GHz_ceiling_run": meas["clock_GHz"], "clock_GHz_after_timed_steps": clock_after,
                 "clock_settle": settle}
     roofline["measured"] = meas
@@ -349,7 +355,7 @@ def main() -> int:
                 a = search_flop(f, wd.shape[0], wd.shape[1], E, odd_groups) / (kern * 1e-3) / 1e12
                 res["search_TFLOP_s"] = round(a, 2)
                 res["roofline_frac"] = frac(a, PEAK_TFLOPS, f"{f} search vs fp32 peak")
-                res["frac_of_measured_fma"] = frac_measured(a, meas["fma_TFLOP_s"])
+                res["frac_of_measured_ceiling"] = frac_measured(a, meas["ceiling_TFLOP_s"])
             return res
 
         per = {}

@@ -57,3 +57,9 @@ def test_fractions_refuse_values_above_one():
         bench.frac(160.0, 157.3, "x")
     assert bench.frac_measured(50.0, 100.0) == 0.5
     assert bench.frac_measured(101.0, 100.0) is None
+
+
+def test_best_ceiling_keeps_the_higher_run():
+    lo = {"ceiling_TFLOP_s": 99.7, "clock_GHz": 1.90}
+    hi = {"ceiling_TFLOP_s": 118.6, "clock_GHz": 2.09}
+    assert bench.best_ceiling(lo, hi) is hi and bench.best_ceiling(hi, lo) is hi
