@@ -491,10 +491,12 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   // chunk of the first-minimum tracking: the every-choice sweeps rescan 16
   // times per lane, so they keep shorter chunks (more bookkeeping, shorter rescans)
   // (IQ1_M takes 16: with 8 its every-choice sweep needs more registers than
-  // four waves per SIMD allow); the 256-entry IQ2_XXS sweep, whose one rescan
-  // weighs more against its short sweep, takes 16
+  // four waves per SIMD allow; IQ2_S takes 16 too: its parity-free 1,024-entry
+  // sweep spends more on the per-chunk bookkeeping than the longer rescans
+  // cost); the 256-entry IQ2_XXS sweep, whose one rescan weighs more against
+  // its short sweep, takes 16
   constexpr bool EV = MODE == EVERY || MODE == RECORDS;
-  constexpr int CH = EV ? (F == IQ1_M ? 16 : 8) : (F == IQ2_XXS ? 16 : 32), NCH = N / CH;
+  constexpr int CH = EV ? (F == IQ1_M || F == IQ2_S ? 16 : 8) : (F == IQ2_XXS ? 16 : 32), NCH = N / CH;
   constexpr int UPW = WGG / GPU;                 // choice units per workgroup
   constexpr int SBS = 32 / WGG;                  // workgroups per block column
   // slots swept per lane: IQ2 16 choices; IQ1 8 scales x 2 shifts;
