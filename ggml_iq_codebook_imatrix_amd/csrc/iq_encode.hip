@@ -474,13 +474,17 @@ __device__ __forceinline__ void stage_grid(const float *__restrict__ grid, float
 // as one word per (choice, group, row) for the choice search.
 enum Mode : int { SEARCH = 0, FIXED_CHOICES = 1, EVERY = 2, RECORDS = 3 };
 
-// Waves per SIMD the compiler must fit: IQ2_S and IQ1_S searches gain from a
-// fifth (measured), the others keep their register budget.
+// Waves per SIMD the compiler must fit (each measured): the IQ1 searches run
+// six (IQ1_M's eight-wave workgroups fit three to a CU instead of two, at the
+// cost of three spilled registers; IQ1_S spills two), IQ2_S five (six spills
+// sixteen registers and runs slower), the others keep their register budget.
 template <int F, int MODE>
 constexpr int search_min_waves() {
-  return (MODE == SEARCH || MODE == FIXED_CHOICES) && (F == IQ2_S || F == IQ1_S) ? 5
-         : F == IQ2_XXS || F == IQ2_XS || F == IQ1_M                                   ? 4
-                                                                                       : 1;
+  constexpr bool SF = MODE == SEARCH || MODE == FIXED_CHOICES;
+  return SF && (F == IQ1_M || F == IQ1_S)              ? 6
+         : SF && F == IQ2_S                            ? 5
+         : F == IQ2_XXS || F == IQ2_XS || F == IQ1_M ? 4
+                                                       : 1;
 }
 
 template <int F, int MODE>
