@@ -184,13 +184,15 @@ def _oracle_importance(orc, x, ids=None, E=1):
     return s_o, c_o, imp_o
 
 
-def test_every_choice_full_size_sampled(api, orc):
-    say("every choice full size IQ2_XS")
-    w, x, grid, spec = inputs.workload("iq2_xs_5632x2048")
+@pytest.mark.parametrize("fmt", ["IQ2_XS", "IQ2_S"])
+def test_every_choice_full_size_sampled(api, orc, fmt):
+    say("every choice full size", fmt)
+    w, x, _, _ = inputs.workload("iq2_xs_5632x2048")
+    grid = inputs.grid_for(fmt, GRID_SEED[fmt])
     _, _, imp = _oracle_importance(orc, x)
-    every = host(api.quantize_every_choice("IQ2_XS", dev_w(w, "bf16"), dev(grid), dev(imp)))
+    every = host(api.quantize_every_choice(fmt, dev_w(w, "bf16"), dev(grid), dev(imp)))
     rid = sample_rows(w.shape[0], 2200)
-    want, _ = orc.quantize_every_choice("IQ2_XS", w, grid, imp, row_ids=rid, threads=THREADS)
+    want, _ = orc.quantize_every_choice(fmt, w, grid, imp, row_ids=rid, threads=THREADS)
     for c in range(want.shape[0]):
         bad = np.argwhere((every[c, rid] != want[c]).any(axis=-1))
         assert bad.size == 0, f"choice {c}: {len(bad)} blocks differ, first {bad[:5].tolist()}"
@@ -298,7 +300,7 @@ def test_choice_search_f32_flat(api, orc, fmt):
     assert np.array_equal(host(pay), pw)
 
 
-@pytest.mark.parametrize("fmt", ["IQ2_XS", "IQ1_M"])
+@pytest.mark.parametrize("fmt", ["IQ2_XS", "IQ2_S", "IQ1_M"])
 def test_choice_search_full_size_sampled(api, orc, fmt):
     """5632x2048 bf16 in the launch configuration bench.py times, with the
     Hessian blocks of the workload's 4,096 tokens (the oracle's, rounded to
