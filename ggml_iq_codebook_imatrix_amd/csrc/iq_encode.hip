@@ -498,11 +498,13 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
   // four waves per SIMD allow; IQ2_S takes 16 too: its parity-free 1,024-entry
   // sweep spends more on the per-chunk bookkeeping than the longer rescans
   // cost); the 256-entry IQ2_XXS sweep, whose one rescan weighs more against
-  // its short sweep, takes 16, and so do the fixed-choice sweeps of IQ2_S and
-  // IQ1_M, which track one slot (two shifts) and so gain less from long chunks
+  // its short sweep, takes 16, as do the IQ2_XS search (measured ~1% faster
+  // than with 32) and the fixed-choice sweeps of IQ2_S and IQ1_M, which track
+  // one slot (two shifts) and so gain less from long chunks
   constexpr bool EV = MODE == EVERY || MODE == RECORDS;
   constexpr int CH = EV ? (F == IQ1_M || F == IQ2_S ? 16 : 8)
-                        : (F == IQ2_XXS || (FIXED && (F == IQ2_S || F == IQ1_M)) ? 16 : 32),
+                        : (F == IQ2_XXS || (!FIXED && F == IQ2_XS) || (FIXED && (F == IQ2_S || F == IQ1_M)) ? 16
+                                                                                                           : 32),
                 NCH = N / CH;
   constexpr int UPW = WGG / GPU;                 // choice units per workgroup
   constexpr int SBS = 32 / WGG;                  // workgroups per block column
