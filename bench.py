@@ -6,7 +6,9 @@ imatrix from 4,096 bf16 tokens (1,024-row chunks) into a 2048-wide statistic,
 turn it into importance, encode the 5632x2048 bf16 weight in the IQ2_XS layout
 (512-entry seeded grid), decode it back to bf16.  Inputs are resident in HBM
 before the timed region.  `value` = encoded elements per second of the whole
-step (M elem/s).
+step (M elem/s).  Before the warm-up steps the chip is brought to the clock it
+holds under this work: 0.25 s of a full-chip FMA stream, the ceiling
+measurement, then 0.1 s of untimed steps (reported as `before_warmup`).
 
 Also reported: the dominant kernel's roofline (the encoder's search kernel,
 timed alone with HIP events around its own launches in every EVENT_STRIDE-th
@@ -201,6 +203,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--settle-s", type=float, default=0.25,
                     help="seconds of full-chip VALU load before the ceiling and the steps (0: none)")
+    ap.add_argument("--step-settle-s", type=float, default=0.1,
+                    help="seconds of untimed steps after the ceiling run, before the warm-up steps (0: none)")
     ap.add_argument("--reps", type=int, default=10, help="repetitions per extra encode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the per-layout / MoE / 17408x5120 tables")
@@ -276,6 +280,20 @@ def main() -> int:
     log("clocks settled", settle)
     meas0 = measured_valu_peak()
     log("measured VALU ceiling (before)", meas0)
+    # the ceiling's FMA streams draw more power than the step, and the clock
+    # they leave behind is below the one the step settles at (the search
+    # kernel measured ~3% slower in the first steps after them), so the step
+    # itself runs untimed for a moment before the warm-up steps
+    step_settle = None
+    if args.step_settle_s > 0:
+        n_settle, ts = 0, time.perf_counter()
+        while n_settle == 0 or time.perf_counter() - ts < args.step_settle_s:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+            n_settle += 8
+        step_settle = {"seconds": round(time.perf_counter() - ts, 3), "steps": n_settle}
+        log("settled on the step", step_settle)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -518,6 +536,8 @@ def main() -> int:
         "config": {"workload": "dense IQ2_XS: collect 4096x2048 bf16 tokens in 1024-row chunks, importance, "
                                "encode + decode a 5632x2048 bf16 weight (512-entry seeded grid)",
                    "rows": rows, "cols": cols, "tokens": T, "format": fmt},
+        # untimed work before the warm-up steps: the ceiling's FMA stream, then the step itself
+        "before_warmup": {"fma_stream": settle, "steps": step_settle},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,
