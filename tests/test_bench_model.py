@@ -63,3 +63,16 @@ def test_best_ceiling_keeps_the_higher_run():
     lo = {"ceiling_TFLOP_s": 99.7, "clock_GHz": 1.90}
     hi = {"ceiling_TFLOP_s": 118.6, "clock_GHz": 2.09}
     assert bench.best_ceiling(lo, hi) is hi and bench.best_ceiling(hi, lo) is hi
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py measures one GPU: asked for more it says so and exits with code 2,
+    before touching torch or a device."""
+    import os
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
