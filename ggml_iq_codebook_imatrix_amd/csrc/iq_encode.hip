@@ -1347,7 +1347,35 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
         }
       }
       __syncthreads();
+      // group by group: the group's weights and cross term are read from LDS
+      // once for all of this wave's choices (each choice's dot product is
+      // still one fmaf chain over the unit's columns in ascending order)
       float dwc[NCW][UV];
+      float dot[NCW];
+#pragma unroll
+      for (int k = 0; k < NCW; ++k) dot[k] = 0.0f;
+#pragma unroll
+      for (int gi = 0; gi < GPU; ++gi) {
+        float xs[8], rs[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xs[j] = s_x[gi * 8 + j][lane];
+          rs[j] = s_r[gi * 8 + j][lane];
+        }
+#pragma unroll
+        for (int k = 0; k < NCW; ++k) {
+          if (v + U * k < NC) {
+            float y[8];
+            if (!EARLY) record_entry(rc[k][gi], A.grid, &gvc[k][gi * 8]);
+            record_finish<F>(d, rc[k][gi], &gvc[k][gi * 8], y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              dwc[k][gi * 8 + j] = xs[j] - y[j];
+              dot[k] = __builtin_fmaf(dwc[k][gi * 8 + j], rs[j], dot[k]);
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int k = 0; k < NCW; ++k) {
         const int c = v + U * k;
@@ -1355,19 +1383,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
           float qu = qk[k][0];
 #pragma unroll
           for (int w = 1; w < U; ++w) qu = u == w ? qk[k][w] : qu;
-          float dot = 0.0f;
-#pragma unroll
-          for (int gi = 0; gi < GPU; ++gi) {
-            float y[8];
-            if (!EARLY) record_entry(rc[k][gi], A.grid, &gvc[k][gi * 8]);
-            record_finish<F>(d, rc[k][gi], &gvc[k][gi * 8], y);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              dwc[k][gi * 8 + j] = s_x[gi * 8 + j][lane] - y[j];
-              dot = __builtin_fmaf(dwc[k][gi * 8 + j], s_r[gi * 8 + j][lane], dot);
-            }
-          }
-          s_f[c][lane] = __builtin_fmaf(2.0f, dot, qu);
+          s_f[c][lane] = __builtin_fmaf(2.0f, dot[k], qu);
         }
       }
       __syncthreads();
