@@ -957,23 +957,31 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint8_t *__restrict__
 // Hessian blocks: lambda = perc_damp * mean(diag H_b), the diagonal summed in
 // fp64 (j ascending) and the mean rounded to fp32.  One wave per block: the
 // lanes fetch the 256 diagonal entries (each in its own cache line) together,
-// then lane 0 walks the running sum from LDS.
+// then lane 0 walks the running sum from LDS.  The same pass flags the blocks
+// no calibration token reached (an all-zero diagonal) for the choice search.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) damping_kernel(const float *__restrict__ hess, float perc_damp,
-                                                      float *__restrict__ lam) {
+                                                      float *__restrict__ lam, uint8_t *__restrict__ reached) {
   __shared__ double s_d[256];
   const int64_t i = blockIdx.x;
   const float *H = hess + i * 65536;
+  bool nonzero = false;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = static_cast<int>(threadIdx.x) + 64 * t;
-    s_d[j] = static_cast<double>(H[j * 257]);
+    const float h = H[j * 257];
+    s_d[j] = static_cast<double>(h);
+    nonzero = nonzero || h != 0.0f;
   }
+  // a calibration token reached the block iff some column's sum of squares
+  // (a diagonal entry) is nonzero
+  const uint64_t any = __ballot(nonzero);
   __syncthreads();
   if (threadIdx.x == 0) {
     double acc = 0.0;
     for (int j = 0; j < 256; ++j) acc += s_d[j];
     lam[i] = perc_damp * static_cast<float>(acc / 256.0);
+    reached[i] = any != 0 ? 1 : 0;
   }
 }
 
@@ -1153,6 +1161,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
                                                                           const uint16_t *__restrict__ dblk,
                                                                           const float *__restrict__ hess,
                                                                           const float *__restrict__ lamv,
+                                                                          const uint8_t *__restrict__ reached,
                                                                           uint8_t *__restrict__ choices) {
   using G = Geo<F>;
   constexpr int U = G::UNITS, UV = 8 * G::GPU, NC = G::NC, GPU = G::GPU;
@@ -1190,6 +1199,88 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
   const int64_t rstride = A.rows;
   const uint32_t *rrow = rec + static_cast<int64_t>(b) * 32 * rstride + r;
   const int64_t cstride = A.nb * 32 * rstride;
+
+  // the picks out, and with A.out the payload under them
+  auto finish = [&](int pick) {
+    if (valid) choices[(r * A.nb + b) * U + v] = static_cast<uint8_t>(pick);
+    if (!A.out) return;
+
+    // payload under the picks: each wave stages its unit's fields (the parts
+    // buffer is free: in the search its last reader is two barriers back, and
+    // the never-reached path below does not use it), then wave sb packs packed
+    // unit sb as the search kernel does
+    constexpr int PG = G::PG, SBS = 32 / PG, UPW = PG / GPU;
+    uint16_t(*p_k)[64] = reinterpret_cast<uint16_t(*)[64]>(s_buf);
+    uint8_t(*p_m)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2);
+    uint8_t(*p_c)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2 + 32 * 64 / 4);
+    const uint16_t d16 = dblk[r * A.nb + b];
+#pragma unroll
+    for (int gi = 0; gi < GPU; ++gi) {
+      const uint32_t wd = rrow[pick * cstride + (v * GPU + gi) * rstride];
+      p_k[v * GPU + gi][lane] = static_cast<uint16_t>(wd & 2047u);
+      p_m[v * GPU + gi][lane] = static_cast<uint8_t>(G::IQ1 ? (wd >> 23) & 1u : (wd >> 11) & 255u);
+    }
+    p_c[v][lane] = static_cast<uint8_t>(d16 ? pick : 0);
+    __syncthreads();
+    if (v < SBS && valid) {
+      uint8_t *blk = A.out + (r * A.nb + b) * G::BYTES;
+      pack_bytes<F>(blk, v, lane, p_k + v * PG, p_m + v * PG, p_c + v * UPW, d16);
+      if (F != IQ1_M && v == 0) *reinterpret_cast<uint16_t *>(blk) = d16;
+    }
+  };
+
+  // R21: a block no calibration token reached (its Hessian diagonal, each
+  // column's sum of squares, all zero: flagged by damping_kernel) keeps the
+  // encoder's own choices.  One flag per block, so the whole workgroup takes
+  // this path.  Each unit scores every choice from the field records with the
+  // fp32 operations of the search's unit scoring: the record under choice c
+  // holds the group's first-minimum entry (and IQ1_M's better shift), whose
+  // reduced error is the slot minimum the search compared.
+  if (!reached[e * A.nb + b]) {
+    float xu[UV], au[UV];
+    unit_weights<F>(A, r, b, v, xu);
+#pragma unroll
+    for (int j = 0; j < UV; ++j)
+      au[j] = A.imp ? A.imp[e * A.cols + static_cast<int64_t>(b) * 256 + v * UV + j] : 1.0f;
+    const float d = f16_bits_to_f32(dblk[r * A.nb + b]);
+    GroupState<F> S[GPU];
+#pragma unroll
+    for (int gi = 0; gi < GPU; ++gi) S[gi].init(xu + gi * 8, au + gi * 8);
+    float bs = 0.0f;
+    int own = 0;
+#pragma unroll 1
+    for (int c = 0; c < NC; ++c) {
+      float score = 0.0f;
+#pragma unroll
+      for (int gi = 0; gi < GPU; ++gi) {
+        const uint32_t rcg = rrow[c * cstride + (v * GPU + gi) * rstride];
+        float g[8];
+        record_entry(rcg, A.grid, g);
+        const float q2 = S[gi].template term<G::PARITY>(g);
+        const float *a = au + gi * 8;
+        float s, t;
+        if (!G::IQ1) {
+          s = d * (static_cast<float>(2 * c + 1) * 0.125f);
+          t = __builtin_fmaf(s, iq2_norm(a, g), q2);
+        } else {
+          const float delta = ((rcg >> 23) & 1u) ? -0.125f : 0.125f;
+          float gh = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float u = g[j] + delta;
+            gh = __builtin_fmaf(a[j], u * u, gh);
+          }
+          s = d * static_cast<float>(2 * (F == IQ1_S ? (c & 7) : c) + 1);
+          t = __builtin_fmaf(s, gh, __builtin_fmaf(delta, S[gi].S2, q2));
+        }
+        const float ev = s * t;
+        score = gi == 0 ? ev : score + ev;
+      }
+      if (c == 0 || score < bs) { bs = score; own = c; }
+    }
+    finish(own);
+    return;
+  }
 
   // step A: every choice of unit v under its own damped block; the U diagonal sub-blocks H_vv ([v][i][j], U * UV * UV = HROW floats) are
   // staged in s_h first
@@ -1413,30 +1504,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::UNITS) choice_search_kernel(EncAr
         for (int gi = 0; gi < GPU; ++gi) rc[k][gi] = rcn[k][gi];
     }
   }
-  if (valid) choices[(r * A.nb + b) * U + v] = static_cast<uint8_t>(pick);
-  if (!A.out) return;
-
-  // payload under the picks: each wave stages its unit's fields (the parts
-  // buffer is free: its last reader is two barriers back), then wave sb packs
-  // packed unit sb as the search kernel does
-  constexpr int PG = G::PG, SBS = 32 / PG, UPW = PG / GPU;
-  uint16_t(*p_k)[64] = reinterpret_cast<uint16_t(*)[64]>(s_buf);
-  uint8_t(*p_m)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2);
-  uint8_t(*p_c)[64] = reinterpret_cast<uint8_t(*)[64]>(s_buf + 32 * 64 / 2 + 32 * 64 / 4);
-  const uint16_t d16 = dblk[r * A.nb + b];
-#pragma unroll
-  for (int gi = 0; gi < GPU; ++gi) {
-    const uint32_t wd = rrow[pick * cstride + (v * GPU + gi) * rstride];
-    p_k[v * GPU + gi][lane] = static_cast<uint16_t>(wd & 2047u);
-    p_m[v * GPU + gi][lane] = static_cast<uint8_t>(G::IQ1 ? (wd >> 23) & 1u : (wd >> 11) & 255u);
-  }
-  p_c[v][lane] = static_cast<uint8_t>(d16 ? pick : 0);
-  __syncthreads();
-  if (v < SBS && valid) {
-    uint8_t *blk = A.out + (r * A.nb + b) * G::BYTES;
-    pack_bytes<F>(blk, v, lane, p_k + v * PG, p_m + v * PG, p_c + v * UPW, d16);
-    if (F != IQ1_M && v == 0) *reinterpret_cast<uint16_t *>(blk) = d16;
-  }
+  finish(pick);
 }
 
 // ---------------------------------------------------------------------------
@@ -1470,7 +1538,8 @@ ChoicePlan plan_choice_search(int fmt, int64_t rows, int64_t cols, int64_t rpe, 
   p.q = plan_quantize(fmt, rows, cols, rpe, weighted);
   p.roff = 0;
   p.loff = ws_up(static_cast<size_t>(kNC[fmt]) * nblocks * 32 * sizeof(uint32_t));
-  p.qoff = p.loff + ws_up(static_cast<size_t>(nl) * sizeof(float));
+  p.foff = p.loff + ws_up(static_cast<size_t>(nl) * sizeof(float));
+  p.qoff = p.foff + ws_up(static_cast<size_t>(nl));
   p.bytes = p.qoff + p.q.bytes;  // the encoder part keeps its own slack
   return p;
 }
@@ -1560,6 +1629,7 @@ static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp,
   char *base = ws_base(ws);
   uint32_t *rec = reinterpret_cast<uint32_t *>(base + P.roff);
   float *lam = reinterpret_cast<float *>(base + P.loff);
+  uint8_t *reached = reinterpret_cast<uint8_t *>(base + P.foff);
   void *qws = base + P.qoff;
   // the record sweep's fp16 block scales, read by the choice search
   const uint16_t *dblk = reinterpret_cast<const uint16_t *>(ws_base(qws) + P.q.doff);
@@ -1569,13 +1639,14 @@ static int launch_choice_search_t(EncArgs A, const float *hess, float perc_damp,
   E.copies = 0;
   E.rec = rec;
   if (launch_quantize_t<F>(E, RECORDS, qws, nullptr, nullptr, stream) != 0) return -1;
-  hipLaunchKernelGGL(damping_kernel, dim3(static_cast<unsigned>(nl)), dim3(64), 0, stream, hess, perc_damp, lam);
+  hipLaunchKernelGGL(damping_kernel, dim3(static_cast<unsigned>(nl)), dim3(64), 0, stream, hess, perc_damp, lam,
+                     reached);
   if (!launched_ok()) return -1;
   A.tiles_per_e = (A.rpe + 63) / 64;
   A.total_wg = A.E * A.tiles_per_e * A.nb;
   hipLaunchKernelGGL(choice_search_kernel<F>, dim3(static_cast<unsigned>(A.total_wg)), dim3(64 * G::UNITS), 0,
                      stream, A, static_cast<const uint32_t *>(rec), dblk, hess, static_cast<const float *>(lam),
-                     choices);
+                     static_cast<const uint8_t *>(reached), choices);
   return launched_ok() ? 0 : -1;
 }
 

@@ -53,7 +53,7 @@ QuantPlan plan_quantize(int fmt, int64_t rows, int64_t cols, int64_t rpe, bool w
 // Choice-search scratch: the field records and damping terms, then an encoder
 // scratch for the record sweep (whose fp16 scales the choice search reads).
 struct ChoicePlan {
-  size_t roff, loff, qoff;   // records, damping terms, encoder scratch
+  size_t roff, loff, foff, qoff;   // records, damping terms, reached flags, encoder scratch
   QuantPlan q;
   size_t bytes;
 };

@@ -568,7 +568,8 @@ void orc_decode_block(int fmt, const uint8_t *in, const float *grid, float *y) {
 /* importance-weighted squared error; with fixed choices the scoring sweep   */
 /* is skipped and the entry search kept.)                                    */
 /* d16_override >= 0 replaces the anchor (used by tests that need an exact   */
-/* lattice scale).  Returns status bits.                                     */
+/* lattice scale).  chosen (may be NULL) receives each unit's choice (0 for  */
+/* an all-zero block).  Returns status bits.                                 */
 /* ------------------------------------------------------------------------- */
 typedef struct {
   float *t;     /* [16][N] reduced errors of one group */
@@ -578,7 +579,8 @@ typedef struct {
 } orc_scratch;
 
 static int encode_block(int fmt, const float *x, const float *a, const float *grid, int N,
-                        const uint8_t *choices, int d16_override, uint8_t *out, orc_scratch *sc) {
+                        const uint8_t *choices, int d16_override, uint8_t *out, orc_scratch *sc,
+                        uint8_t *chosen) {
   const orc_geom *G = &GEOM[fmt];
   int st = 0;
   uint16_t d16;
@@ -596,7 +598,11 @@ static int encode_block(int fmt, const float *x, const float *a, const float *gr
   if (choices)
     for (int u = 0; u < G->units; ++u)
       if (choices[u] >= G->nchoices) { st |= ORC_ST_BADCHOICE; d16 = 0; }
-  if (d16 == 0) { memset(out, 0, (size_t)G->block_bytes); return st; }
+  if (d16 == 0) {
+    memset(out, 0, (size_t)G->block_bytes);
+    if (chosen) memset(chosen, 0, (size_t)G->units);
+    return st;
+  }
   float d = orc_f16_to_f32(d16);
   int flips[32][16];
 
@@ -665,6 +671,7 @@ static int encode_block(int fmt, const float *x, const float *a, const float *gr
       }
     }
     f.ls[u] = (fmt == ORC_IQ1_S) ? (cu & 7) : cu;
+    if (chosen) chosen[u] = (uint8_t)cu;
   }
   orc_pack(fmt, &f, out);
   return st;
@@ -684,7 +691,7 @@ int orc_encode_block(int fmt, const float *x, const float *a, const float *grid,
   if (fmt < 0 || fmt > 4 || grid_n < 1) return -1;
   orc_scratch sc;
   scratch_init(&sc, grid_n);
-  int st = encode_block(fmt, x, a, grid, grid_n, choices, d16_override, out, &sc);
+  int st = encode_block(fmt, x, a, grid, grid_n, choices, d16_override, out, &sc, NULL);
   scratch_free(&sc);
   return st;
 }
@@ -739,7 +746,7 @@ static void *quantize_rows(void *p) {
       const float *a = J->imp ? J->imp + e * J->cols + b * 256 : ones;
       const uint8_t *ch = J->choices ? J->choices + (r * nb + b) * G->units : NULL;
       uint8_t *o = J->out + (i * nb + b) * G->block_bytes;
-      J->st |= encode_block(J->fmt, x, a, J->grid, G->grid_n, ch, -1, o, &sc);
+      J->st |= encode_block(J->fmt, x, a, J->grid, G->grid_n, ch, -1, o, &sc, NULL);
     }
   }
   free(ones);
@@ -795,7 +802,10 @@ int orc_dequantize(int fmt, const uint8_t *packed, int64_t rows, int64_t cols, c
 /* other units v of H_uv dw_v at the current picks, gathered unit by unit:    */
 /* each unit's contribution is an fmaf chain over its columns (ascending,     */
 /* from zero) and the contributions are added in ascending unit order; a pick */
-/* takes effect at once (units visited in ascending order).                   */
+/* takes effect at once (units visited in ascending order).  R21 a block no   */
+/* calibration token reached (its Hessian diagonal, each column's sum of      */
+/* squares, all zero) keeps the encoder's own choices ([3158] Testing: a      */
+/* never-reached weight is encoded plainly).                                  */
 /* ------------------------------------------------------------------------- */
 static float hd(const float *H, float lam, int i, int j) {
   float v = H[i * 256 + j];
@@ -831,9 +841,20 @@ static int choice_search_block(int fmt, const float *x, const float *a, const fl
   int st = 0;
   for (int c = 0; c < NC; ++c) {
     for (int u = 0; u < U; ++u) ch[u] = (uint8_t)c;
-    st |= encode_block(fmt, x, a, grid, G->grid_n, ch, -1, blk, sc);
+    st |= encode_block(fmt, x, a, grid, G->grid_n, ch, -1, blk, sc, NULL);
     orc_decode_block(fmt, blk, grid, yhat);
     for (int j = 0; j < 256; ++j) dwc[c * 256 + j] = x[j] - yhat[j];
+  }
+  /* R21 ([3158] Testing: a never-reached weight is encoded plainly): a block
+   * no calibration token reached -- every column's sum of squares, the
+   * Hessian's diagonal, is zero -- keeps the encoder's own choices. */
+  int reached = 0;
+  for (int j = 0; j < 256; ++j)
+    if (H[j * 256 + j] != 0.0f) reached = 1;
+  if (!reached) {
+    st |= encode_block(fmt, x, a, grid, G->grid_n, NULL, -1, blk, sc, choices);
+    free(dwc);
+    return st;
   }
   const float lam = orc_damping(H, perc_damp);
   int pick[16];

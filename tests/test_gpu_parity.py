@@ -286,6 +286,37 @@ def test_choice_search_adversarial_hessian(api, orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+def test_choice_search_never_reached_blocks(api, orc, fmt):
+    """R21 ([3158] Testing: a never-reached weight is encoded plainly): expert
+    0's blocks and expert 1's first block have all-zero Hessians; their picks
+    are the oracle's and their payload is the device's own plain encode
+    (iq_quantize) byte for byte; expert 1's second block is searched.  Ragged
+    70-row experts, bf16 weights."""
+    say("choice search never-reached blocks", fmt)
+    g = inputs.rng(2800 + FORMATS.index(fmt))
+    grid = inputs.grid_for(fmt, GRID_SEED[fmt])
+    rpe, cols = 70, 512
+    w = inputs.weight(2 * rpe, cols, 2801, 2802, bf16=True)
+    imp = np.stack([np.ones(cols, np.float32), inputs.importance_like(cols, 2803)])
+    hess = np.zeros((2, 2, 256, 256), np.float32)
+    x = g.standard_normal((64, 256)).astype(np.float32)
+    hess[1, 1] = (x.T.astype(np.float64) @ x.astype(np.float64)).astype(np.float32)
+    wd = dev_w(w, "bf16")
+    got, pay = api.choice_search(fmt, wd, dev(grid), dev(hess), dev(imp), rows_per_expert=rpe, perc_damp=0.3,
+                                 payload=True)
+    plain = host(api.quantize(fmt, wd, dev(grid), dev(imp), rows_per_expert=rpe))
+    got, pay = host(got), host(pay)
+    want, _ = orc.choice_search(fmt, w, grid, hess, imp, rows_per_expert=rpe, perc_damp=0.3)
+    assert np.array_equal(got, want)
+    pw, _ = orc.quantize(fmt, w, grid, imp, rows_per_expert=rpe, choices=want)
+    assert np.array_equal(pay, pw)
+    unreached = np.zeros((2 * rpe, 2), bool)
+    unreached[:rpe, :] = True
+    unreached[rpe:, 0] = True
+    assert np.array_equal(pay[unreached], plain[unreached])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_choice_search_f32_flat(api, orc, fmt):
     """fp32 weights, flat importance, a ragged 64-row tile, one block column."""
     say("choice search f32 flat", fmt)

@@ -13,6 +13,10 @@
   damps) equals numpy's evaluation of that definition, and under a
   block-diagonal Hessian, where every unit is independent, the damped picks are
   the fp64 minimisers of dw (H + lambda I) dw^T wherever the margin is clear.
+* A block no calibration token reached (R21: an all-zero Hessian diagonal) is
+  encoded plainly: its payload under the search's picks is the encoder's own
+  ("encodes a never-reached weight plainly"), while a block with one nonzero
+  diagonal entry is searched.
 """
 import numpy as np
 import pytest
@@ -249,3 +253,40 @@ def test_damped_picks_are_fp64_minimisers_under_block_diagonal_h(orc, fmt):
             wrong, clear_w = fp64_picks(p * diag.max())
             assert (wrong[clear & clear_w] != got[clear & clear_w]).any()
     assert seen_change > 0
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("perc_damp", [0.0, 0.3])
+def test_never_reached_block_is_encoded_plainly(orc, fmt, perc_damp):
+    """[3158] Testing: a never-reached weight is encoded plainly.  Expert 0's
+    blocks and expert 1's first block have all-zero Hessians (no token reached
+    them): their payload under the picks is the importance-weighted encode's
+    own, byte for byte, and the picks are its own choices.  (Left to the
+    search's rule, an all-zero block would score every choice 0 and take
+    choice 0 everywhere.)  Expert 1's second block is reached and searched."""
+    g = inputs.rng(3700 + FORMATS.index(fmt))
+    rpe, cols = 5, 512
+    w = inputs.weight(2 * rpe, cols, 3701, 3702, bf16=False)
+    grid = inputs.grid_for(fmt, 3703)
+    imp = np.stack([np.ones(cols, np.float32), inputs.importance_like(cols, 3704)])
+    hess = np.zeros((2, 2, 256, 256), np.float32)
+    x = g.standard_normal((40, 256)).astype(np.float32)
+    hess[1, 1] = (x.T.astype(np.float64) @ x.astype(np.float64)).astype(np.float32)
+    picks, _ = orc.choice_search(fmt, w, grid, hess, imp, rows_per_expert=rpe, perc_damp=perc_damp)
+    plain, _ = orc.quantize(fmt, w, grid, imp, rows_per_expert=rpe)
+    under, _ = orc.quantize(fmt, w, grid, imp, rows_per_expert=rpe, choices=picks)
+    unreached = np.zeros((2 * rpe, 2), bool)
+    unreached[:rpe, :] = True
+    unreached[rpe:, 0] = True
+    assert np.array_equal(under[unreached], plain[unreached])
+    assert np.array_equal(picks[unreached], own_choices(orc, fmt, plain)[unreached])
+    # choice 0 everywhere would not be the plain encode here
+    assert np.any(picks[unreached] != 0)
+    # one nonzero diagonal entry: the block is reached and searched (under a
+    # single nonzero entry the error is that column's alone, so the other
+    # units' own blocks are all zero and every choice ties: choice 0)
+    h1 = np.zeros((1, 1, 256, 256), np.float32)
+    h1[0, 0, 255, 255] = 1.0
+    p1, _ = orc.choice_search(fmt, w[:1, :256], grid, h1, imp[1:2, :256], perc_damp=0.0)
+    geo = orc.geometry(fmt)
+    assert np.all(p1[0, 0, :geo["units"] - 1] == 0)
