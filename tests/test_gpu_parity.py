@@ -317,6 +317,32 @@ def test_choice_search_never_reached_blocks(api, orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+def test_imatrix_output_error_beats_plain_encode(api, orc, fmt):
+    """[imatrix PR] unit tests, on the device path end to end: bf16 tokens
+    collected and turned into importance, the weight encoded with it and flat,
+    both decoded; the layer-output error ||X (W - W^)^T||^2 of the imatrix
+    encode is below the plain encode's on every row.  Both payloads equal the
+    oracle's on the device's importance."""
+    say("imatrix output error", fmt)
+    rows, cols, T = 48, 512, 768
+    w = inputs.weight(rows, cols, 3801, 3802, bf16=True)
+    x = inputs.activations(T, cols, 3803, 3804, bf16=True)
+    grid = inputs.grid_for(fmt, 3805)
+    wd, gd = dev_w(w, "bf16"), dev(grid)
+    sums, counts = api.imatrix_collect(dev_w(x, "bf16"))
+    imp = api.imatrix_importance(sums, counts)
+    X = x.astype(np.float64)
+    err = {}
+    for k, im in (("imatrix", imp), ("plain", None)):
+        p = api.quantize(fmt, wd, gd, im)
+        y = host(api.dequantize(fmt, p, gd)).astype(np.float64)
+        want, _ = orc.quantize(fmt, w, grid, None if im is None else host(im))
+        assert np.array_equal(host(p), want)
+        err[k] = ((X @ (w.astype(np.float64) - y).T) ** 2).sum(axis=0)
+    assert np.all(err["imatrix"] < err["plain"])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_choice_search_f32_flat(api, orc, fmt):
     """fp32 weights, flat importance, a ragged 64-row tile, one block column."""
     say("choice search f32 flat", fmt)

@@ -11,6 +11,8 @@
   "a fixed choice reproduces, group by group, the payload encoded with that
   choice everywhere").
 * Importance-weighted error never exceeds the flat-weight encode's.
+* The imatrix encode's layer-output error beats the plain encode's (the imatrix
+  PR's unit test), on every row.
 """
 import numpy as np
 import pytest
@@ -291,3 +293,28 @@ def test_exact_choice_and_shift_ties(orc, fmt):
             assert np.all(f["h"] == want["h"])
         ls = (b["choice"] & 7) if fmt == "IQ1_S" else b["choice"]
         assert np.array_equal(f["ls"][:U], ls) and np.array_equal(f["k"], b["k"])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_imatrix_output_error_beats_plain_encode(orc, fmt):
+    """[imatrix PR] unit tests: the imatrix encode's output error beats the
+    plain encode.  Tokens with lognormal column scales (the workloads' recipe),
+    the statistic collected from them, importance its floored square root;
+    the layer-output error ||X (W - W^)^T||^2 (fp64, from the decoded weights)
+    of the importance-weighted encode is below the flat encode's on every row
+    and well below it in total."""
+    rows, cols, T = 48, 512, 768
+    w = inputs.weight(rows, cols, 3801, 3802, bf16=False)
+    x = inputs.activations(T, cols, 3803, 3804, bf16=False)
+    grid = inputs.grid_for(fmt, 3805)
+    s, c, _ = orc.collect(x)
+    imp, _ = orc.importance(s.astype(np.float32), c)
+    p_i, _ = orc.quantize(fmt, w, grid, imp)
+    p_f, _ = orc.quantize(fmt, w, grid, None)
+    X = x.astype(np.float64)
+    err = {}
+    for k, p in (("imatrix", p_i), ("plain", p_f)):
+        y = orc.dequantize(fmt, p, rows, cols, grid).astype(np.float64)
+        err[k] = ((X @ (w.astype(np.float64) - y).T) ** 2).sum(axis=0)  # per row
+    assert np.all(err["imatrix"] < err["plain"])
+    assert err["imatrix"].sum() < 0.7 * err["plain"].sum()
