@@ -270,6 +270,10 @@ int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, in
  *  perc_damp  H_b + perc_damp * mean(diag H_b) * I is used (0.3 in [3158]).
  *  choices  (device) [rows, cols/256, choice_groups] uint8 OUT: the picks, to be
  *           passed to iq_quantize (IQ1_S: (delta_sign << 3) | local scale).
+ *           A block no calibration token reached (all-zero diag H_b, e.g. an
+ *           idle expert's) keeps the encoder's own choices, so its payload is
+ *           iq_quantize's ([3158] Testing: a never-reached weight is encoded
+ *           plainly).
  *  out      (device, nullable) [rows, cols/256, block_bytes] uint8 OUT: when
  *           given, the payload under the picks -- byte for byte what iq_quantize
  *           writes with `choices` -- packed from the every-choice fields the
@@ -277,7 +281,7 @@ int iq_quantize_every_choice(int fmt, const void *w, int dtype, int64_t rows, in
  *  workspace, workspace_bytes  (device) scratch of at least
  *           iq_choice_search_workspace_size(...) bytes: every group's fields
  *           under every choice (num_choices * rows * cols/8 * 4 bytes), the
- *           damping terms and an encoder workspace.
+ *           damping terms, the reached flags and an encoder workspace.
  *  importance, grid, w, rows_per_expert, status: as iq_quantize (the codebook
  *  search keeps the importance weighting).
  * Errors: as iq_quantize, plus IQ_ERR_NULL (hess, choices) and IQ_ERR_ARG
