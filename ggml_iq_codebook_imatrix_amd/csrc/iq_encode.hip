@@ -769,33 +769,45 @@ __global__ void __launch_bounds__(64 * Geo<F>::WGG, (search_min_waves<F, MODE>()
     cu = fixed_c;
     slot = (F == IQ1_M) ? (best[1] < best[0] ? 1 : 0) : 0;
   } else {
+    // each (unit, row) is scored once: wave p < UPW scores unit p for row
+    // lane (the unit's other groups would repeat the same sums) and hands the
+    // choice to the unit's items through LDS; the row's block scale comes
+    // through LDS too, since a lane's item row need not be its lane's row
+    __shared__ float s_drow[64];
+    __shared__ uint8_t s_cu[UPW][64];
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) s_best[gw][s][rl] = best[s];
+    if (gw == 0) s_drow[rl] = d;
     __syncthreads();
-    float bs = 0.0f;
+    if (wave < UPW) {
+      const float dr = s_drow[lane];
+      float bs = 0.0f;
+      int cs = 0;
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c) {
-      float score = 0.0f;
+      for (int c = 0; c < G::NC; ++c) {
+        // the slot scales as the sweep formed them (sc[] of the row)
+        const float s = G::IQ1 ? dr * static_cast<float>(2 * (F == IQ1_S ? (c & 7) : c) + 1)
+                               : dr * (static_cast<float>(2 * c + 1) * 0.125f);
+        float score = 0.0f;
 #pragma unroll
-      for (int i = 0; i < GPU; ++i) {
-        const int w = uw * GPU + i;
-        float bb, s;
-        if (F == IQ1_M) {
-          const float b0 = s_best[w][c][rl], b1 = s_best[w][8 + c][rl];
-          bb = (b1 < b0) ? b1 : b0;          // tie: the lower shift
-          s = sc[c];
-        } else if (F == IQ1_S) {
-          bb = s_best[w][c][rl];
-          s = sc[c & 7];
-        } else {
-          bb = s_best[w][c][rl];
-          s = sc[c];
+        for (int i = 0; i < GPU; ++i) {
+          const int w = wave * GPU + i;
+          float bb;
+          if (F == IQ1_M) {
+            const float b0 = s_best[w][c][lane], b1 = s_best[w][8 + c][lane];
+            bb = (b1 < b0) ? b1 : b0;          // tie: the lower shift
+          } else {
+            bb = s_best[w][c][lane];
+          }
+          const float ev = s * bb;
+          score = (i == 0) ? ev : score + ev;
         }
-        const float ev = s * bb;
-        score = (i == 0) ? ev : score + ev;
+        if (c == 0 || score < bs) { bs = score; cs = c; }
       }
-      if (c == 0 || score < bs) { bs = score; cu = c; }
+      s_cu[wave][lane] = static_cast<uint8_t>(cs);
     }
+    __syncthreads();
+    cu = s_cu[uw][rl];
     if (F == IQ1_M) {
       float b0 = best[0], b1 = best[8];
 #pragma unroll
